@@ -1,0 +1,2 @@
+"""Seeded synthetic workloads (inputs only, none of the method's arithmetic)."""
+from .synth import WORKLOADS, Workload, make_inputs, append_token, draw_seq_lens  # noqa: F401
