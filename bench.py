@@ -1,0 +1,315 @@
+"""Benchmark of the SeerAttention-R decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole decode hot path over one batch: K
+Compression Cache update, gate scores, block selection and block-sparse
+decode with its split merge.  The default workload is the Qwen3-14B-shaped
+batch (16 sequences, 40 query / 8 KV heads, d = 128, 32k context, 64-token
+blocks, top-k 52 of 512 blocks = 90% sparsity).  Inputs are synthetic and
+already resident in HBM.  To keep the 256 MB Infinity Cache from serving
+repeated reads, the timed loop cycles through several independent replicas
+of the inputs (each step touches a different one).
+
+Prints one JSON line: µs per step (lower is better), achieved HBM bandwidth
+of the decode kernel on its algorithmic bytes against the 8 TB/s peak, the
+speedup over the library's own dense decode at equal shape, and the float64
+oracle timed on the host cores on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("sparse decode µs/step + achieved HBM GB/s (% peak); "
+          "speedup vs dense @90% sparsity")
+PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_seer_amd", "csrc", "decode.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_src_hash() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None if they are absent or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_src_sha256_16") != decode_src_hash():
+        return None
+    return t
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_14b_b16")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--dense-steps", type=int, default=20)
+    ap.add_argument("--num-split", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the decode path of one layer is measured on a "
+              "single MI355X (no multi-GPU path is built); use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_seer_amd as S
+    from workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    S.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    if w.seq_len is None:
+        print("bench.py times single-length workloads (qwen3_8b_layer, qwen3_14b_b16, tiny)",
+              file=sys.stderr)
+        return 2
+    B, Hq, Hkv, d, dg, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate, w.block_size
+    g = w.group
+    L = w.seq_len
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
+    mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
+
+    # ---- replicas of the inputs, each with its own cache and step buffers
+    R = max(1, args.replicas)
+    reps = []
+    for r in range(R):
+        log(f"generating replica {r + 1}/{R}")
+        inp = make_inputs(w.replace(seed=w.seed + 7919 * r), device=str(dev))
+        st = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau,
+                          num_split=args.num_split, device=dev)
+        seq = inp["seq_lens"]
+        st.build_cache(inp["k"], inp["w_k"], seq)
+        reps.append((inp, st))
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+
+    def step(r, ev=None):
+        inp, st = reps[r]
+        seq = inp["seq_lens"]
+        S.seer_kcomp_update(dims, inp["k"], inp["w_k"], seq, st.kcomp_lens, st.kcomp, 1, w.theta)
+        S.seer_gate_scores(dims, inp["q"], inp["w_q"], st.kcomp, st.kcomp_lens, seq, st.gate_ws,
+                           st.logits, w.theta)
+        S.seer_select_blocks(dims, st.logits, st.kcomp_lens, seq, mode, w.topk_blocks, w.tau,
+                             st.max_selected, st.block_idx, st.num_selected)
+        if ev is not None:
+            ev[0].record()
+        S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], seq, st.block_idx,
+                             st.num_selected, st.max_selected, scale, st.num_split, st.decode_ws,
+                             st.out, st.lse)
+        if ev is not None:
+            ev[1].record()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_us = 1e3 * float(np.mean(dec_ms))
+    dec_us_med = 1e3 * float(np.median(dec_ms))
+
+    # ---- algorithmic bytes (per step, from the actual selections)
+    sel_tokens = []
+    nb = L // bs
+    for inp, st in reps:
+        ns = st.num_selected.cpu().numpy()
+        idx = st.block_idx.cpu().numpy()
+        tot = 0
+        for b_ in range(B):
+            for h_ in range(Hkv):
+                for j in idx[b_, h_, :ns[b_, h_]]:
+                    tot += min(bs, L - int(j) * bs)
+        sel_tokens.append(tot)
+    sel_tokens = float(np.mean(sel_tokens))
+    qo_bytes = 2 * B * Hq * d * 2
+    kv_bytes = sel_tokens * 2 * d * 2
+    idx_bytes = B * Hkv * (reps[0][1].max_selected + 1) * 4
+    decode_alg = kv_bytes + qo_bytes + idx_bytes
+    step_alg = decode_alg + B * Hkv * nb * dg * 2 + Hkv * dg * g * d * 2
+    achieved = decode_alg / (dec_us * 1e-6) / 1e9
+    step_gbps = step_alg / (ms_per_step * 1e-3) / 1e9
+
+    # ---- dense baseline at equal shape
+    log(f"dense baseline {args.dense_steps} steps")
+    ns_dense = S.seer_decode_num_split(dims, dims.nb_max, 0)
+    dws = torch.zeros(max(S.seer_decode_workspace_bytes(dims, dims.nb_max, ns_dense), 256) // 4 + 64,
+                      dtype=torch.float32, device=dev)
+    dout = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+    def dense(r):
+        inp, _ = reps[r]
+        S.seer_dense_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], scale, ns_dense,
+                            dws, dout, dlse)
+
+    for i in range(3):
+        dense(i % R)
+    torch.cuda.synchronize()
+    dev_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.dense_steps)]
+    for i in range(args.dense_steps):
+        dev_evs[i][0].record()
+        dense(i % R)
+        dev_evs[i][1].record()
+    torch.cuda.synchronize()
+    dense_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in dev_evs]))
+    dense_bytes = B * Hkv * L * 2 * d * 2 + qo_bytes
+    dense_gbps = dense_bytes / (dense_us * 1e-6) / 1e9
+
+    # ---- amortised cost of a real cache update (one block per (b, h))
+    inp0, st0 = reps[0]
+    kupd = []
+    for i in range(5):
+        st0.kcomp_lens.fill_(nb - 1)
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        S.seer_kcomp_update(dims, inp0["k"], inp0["w_k"], inp0["seq_lens"], st0.kcomp_lens,
+                            st0.kcomp, 1, w.theta)
+        b_.record()
+        torch.cuda.synchronize()
+        kupd.append(a_.elapsed_time(b_) * 1e3)
+    kcomp_us = float(np.median(kupd))
+
+    # ---- float64 oracle on the host cores, bounded sample
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(reps[0][0], w, args.cpu_seconds)
+
+    traffic = measured_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "d_gate": dg, "block_size": bs, "seq_len": L, "mode": w.mode,
+                   "topk_blocks": w.topk_blocks, "num_split": reps[0][1].num_split,
+                   "replicas": R},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel (block-sparse split decode + LSE merge)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
+            "algorithmic_bytes": int(decode_alg),
+            "avg_launch_us": round(dec_us, 3),
+            "median_launch_us": round(dec_us_med, 3),
+        },
+        "step_algorithmic_bytes": int(step_alg),
+        "step_GBps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / PEAK_GBPS, 4),
+        "dense_us": round(dense_us, 2),
+        "dense_GBps": round(dense_gbps, 1),
+        "speedup_vs_dense_step": round(dense_us / (ms_per_step * 1e3), 3),
+        "speedup_vs_dense_kernel": round(dense_us / dec_us, 3),
+        "kcomp_update_us_per_completion": round(kcomp_us, 2),
+        "kcomp_update_us_amortised": round(kcomp_us / bs, 3),
+        "selected_fraction": round(sel_tokens / (B * Hkv * L), 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(inp, w, budget_s):
+    """The float64 oracle's decode step (gate query, logits, selection,
+    attention; its cache prebuilt and untimed) on sampled (b, h) pairs,
+    scaled to µs per full step."""
+    import numpy as np
+
+    import oracle as O
+
+    f = lambda t: t.detach().double().cpu().numpy()  # noqa: E731
+    L = w.seq_len
+    g = w.group
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(pairs))
+    log("cpu baseline: preparing sampled pairs")
+    prepared = []
+    t_prep = time.perf_counter()
+    for i in order[:8]:
+        b, h = pairs[i]
+        k = f(inp["k"][b, h, :L])
+        kc = O.build_kcomp(k, f(inp["w_k"][h]), L, w.block_size, w.theta)
+        prepared.append((f(inp["q"][b, h * g:(h + 1) * g]), k, f(inp["v"][b, h, :L]),
+                         f(inp["w_q"][h]), kc))
+        if time.perf_counter() - t_prep > budget_s:
+            break
+    times = []
+    t_start = time.perf_counter()
+    n = 0
+    while True:
+        q, k, v, wq, kc = prepared[n % len(prepared)]
+        t0 = time.perf_counter()
+        O.decode_pair(q, q, k, k, v, wq, kc, L, w.block_size, mode=w.mode, topk=w.topk_blocks,
+                      tau=w.tau, scale=1.0 / math.sqrt(w.head_dim), theta=w.theta)
+        times.append(time.perf_counter() - t0)
+        n += 1
+        if time.perf_counter() - t_start > budget_s and n >= len(prepared):
+            break
+    per_pair = float(np.median(times))
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(per_pair * len(pairs) * 1e6, 1), "unit": "us/step", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} oracle pair-steps over {len(prepared)} sampled (b, h) pairs of "
+                      f"{len(pairs)}; median pair time x {len(pairs)} pairs; NumPy float64, "
+                      f"BLAS threads at default"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

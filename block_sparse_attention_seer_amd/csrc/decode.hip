@@ -1,0 +1,404 @@
+// Block-sparse flash decoding with split-KV and a log-sum-exp merge, for
+// gfx950 (MI355X).
+//
+// [CP Knowl 6] (chapterpal page "SeerAttention-R: Sparse Attention
+// Adaptation for Long Reasoning"): the kernel runs over a (batch, heads_kv,
+// num_split) grid, divides each (batch, KV head)'s work along num_split
+// using its list of active blocks rather than the sequence's block count,
+// and visits only the active block indices, skipping invalid entries.
+// [PN key design 4] (papernotes page "Sparse Attention Adaptation for Long
+// Reasoning"): the same flash-decoding schedule along the GQA group.
+//
+// MI355X design (not the pages' H100 design):
+//   * one workgroup = 4 waves = one split of one (b, h); a wave walks every
+//     4th 64-token chunk of the split and keeps its own online softmax;
+//   * both contractions run on MFMA v_mfma_f32_16x16x32_bf16 with the g
+//     query heads of the group padded to 16:
+//       S^T[token][head] = K[token][:] . q[head][:]      (A = K rows straight
+//                                                         from HBM, B = q)
+//       O[head][dim]    += P[head][token] V[token][dim]  (A = P from the S
+//                                                         accumulators, B = V)
+//     The score accumulators already sit in the P operand's layout, so P
+//     never leaves registers.  V is loaded as 8-byte pieces (4 dims of one
+//     token) and the B operand (8 tokens of one dim) is assembled with
+//     byte permutes, so V never goes through LDS;
+//   * the 4 waves merge in LDS; the splits of a (b, h) merge in the same
+//     launch: the last workgroup to finish (device-scope counter) combines
+//     the per-split (lse, o) partials.
+#include "seer_device.hpp"
+#include "seer_internal.h"
+
+namespace seer {
+
+namespace {
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq_lens;
+  const int32_t* block_idx;
+  const int32_t* num_selected;
+  int32_t* counters;
+  float* part_lse;
+  float* part_o;
+  uint16_t* out;
+  float* lse;
+  int64_t sb, sh;
+  int st;
+  int Hq, Hkv, G, Lmax, max_sel, num_split;
+  float scale_log2;  // softmax scale times log2(e): scores are kept in log2 units
+};
+
+constexpr int kWaves = 4;
+
+// Element j (0..3) of four packed bf16 values.
+__device__ __forceinline__ uint32_t pick2(uint2 a, uint2 b, int j) {
+  // returns bf16 j of a in the low half and bf16 j of b in the high half
+  const uint32_t x = (j < 2) ? a.x : a.y;
+  const uint32_t y = (j < 2) ? b.x : b.y;
+  return (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+}
+
+template <int D, int BS, bool DENSE>
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+  constexpr int KS = D / 32;   // k-steps of the score contraction
+  constexpr int VH = D / 64;   // 64-dim halves of the value contraction
+  constexpr int CPB = BS / 64; // 64-token chunks per block
+
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+  __shared__ float sm_o[kWaves][16][D];
+  __shared__ float sm_lse[16];
+  __shared__ int sm_last;
+
+  const int S = p.num_split;
+  const int pair = blockIdx.x / S;
+  const int split = blockIdx.x - pair * S;
+  const int b = pair / p.Hkv;
+  const int h = pair - b * p.Hkv;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int ln = lane & 15;
+  const int lq = lane >> 4;
+  const int G = p.G;
+
+  int L = p.seq_lens[b];
+  L = min(max(L, 0), p.Lmax);
+  const int nblk = (L + BS - 1) / BS;
+  int nslots;
+  if (DENSE) {
+    nslots = nblk;
+  } else {
+    nslots = p.num_selected[pair];
+    nslots = min(max(nslots, 0), p.max_sel);
+  }
+  const int C = nslots * CPB;
+  const int per = (C + S - 1) / S;
+  const int c0 = split * per;
+  const int c1 = min(C, c0 + per);
+
+  const uint16_t* kb = p.k + b * p.sb + h * p.sh;
+  const uint16_t* vb = p.v + b * p.sb + h * p.sh;
+  const int32_t* idx = DENSE ? nullptr : p.block_idx + static_cast<int64_t>(pair) * p.max_sel;
+
+  // q of head ln as the B operand of the score MFMA (zero for padding heads).
+  uint4 qop[KS];
+  {
+    const uint16_t* qb = p.q + (static_cast<int64_t>(b) * p.Hq + h * G) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qop[s] = (ln < G) ? ld16(qb + ln * D + 32 * s + 8 * lq) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  float m_run = -INFINITY;  // running max of head ln (log2 units)
+  float l_run = 0.f;        // running sum over this lane's tokens of head ln
+  f32x4_t oacc[VH * 4];
+#pragma unroll
+  for (int t = 0; t < VH * 4; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = c0 + w; c < c1; c += kWaves) {
+    const int slot = c / CPB;
+    const int sub = c - slot * CPB;
+    const int blk = DENSE ? slot : idx[slot];
+    if (blk < 0 || blk >= nblk) continue;  // invalid entry: skipped
+    const int t0 = blk * BS + sub * 64;
+    if (t0 >= L) continue;
+    const int last = L - 1;
+
+    // K rows 16*nt + ln, dims 32*s + 8*lq .. +7 (the A operand).
+    uint4 kr[4][KS];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int row = min(t0 + 16 * nt + ln, last);
+      const uint16_t* kp = kb + row * p.st + 8 * lq;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kr[nt][s] = ld16(kp + 32 * s);
+    }
+    // V rows 16*nt + 4*lq + r, dims 64*hh + 4*ln .. +3.
+    uint2 vr[4][4][VH];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(t0 + 16 * nt + 4 * lq + r, last);
+        const uint16_t* vp = vb + row * p.st + 4 * ln;
+#pragma unroll
+        for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = ld8(vp + 64 * hh);
+      }
+    // Keep all K and V loads of the chunk in flight together: nothing below
+    // may be scheduled above this point.
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Scores: sc[nt][r] = S[token t0 + 16 nt + 4 lq + r][head ln].
+    f32x4_t sc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) sc[nt] = mfma16x16x32(kr[nt][s], qop[s], sc[nt]);
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = t0 + 16 * nt + 4 * lq + r;
+        float x = sc[nt][r] * p.scale_log2;
+        x = (tok <= last) ? x : -INFINITY;
+        sc[nt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the chunk has a valid token
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+
+    // Probabilities, rounded to bf16 once; the row sum uses the rounded
+    // values so that O is an exact convex combination of the V rows.
+    uint32_t pk[4][2];
+    float psum = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const float p0 = fast_exp2(sc[nt][2 * rr] - m_new);
+        const float p1 = fast_exp2(sc[nt][2 * rr + 1] - m_new);
+        const uint32_t u = f2bf2(p0, p1);
+        pk[nt][rr] = u;
+        psum += bf_lo(u) + bf_hi(u);
+      }
+    l_run = l_run * alpha + psum;
+
+    // Rescale the O rows: row 4*lq + r2 belongs to head 4*lq + r2, whose
+    // alpha sits in lane 4*lq + r2.
+#pragma unroll
+    for (int r2 = 0; r2 < 4; ++r2) {
+      const float a = __shfl(alpha, 4 * lq + r2);
+#pragma unroll
+      for (int t = 0; t < VH * 4; ++t) oacc[t][r2] *= a;
+    }
+
+    // O[head][64 hh + 4 ln + j] += P[head][tokens] . V[tokens][..]; the 8
+    // tokens of k-group lq in step s2 are 16*(2 s2 + kk/4) + 4 lq + kk%4.
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint4 pa = make_uint4(pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]);
+#pragma unroll
+      for (int hh = 0; hh < VH; ++hh)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint4 vbop;
+          vbop.x = pick2(vr[2 * s2][0][hh], vr[2 * s2][1][hh], j);
+          vbop.y = pick2(vr[2 * s2][2][hh], vr[2 * s2][3][hh], j);
+          vbop.z = pick2(vr[2 * s2 + 1][0][hh], vr[2 * s2 + 1][1][hh], j);
+          vbop.w = pick2(vr[2 * s2 + 1][2][hh], vr[2 * s2 + 1][3][hh], j);
+          oacc[hh * 4 + j] = mfma16x16x32(pa, vbop, oacc[hh * 4 + j]);
+        }
+    }
+  }
+
+  // ---- merge the 4 waves of this split
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (lq == 0) {
+    sm_m[w][ln] = m_run;
+    sm_l[w][ln] = l_run;
+  }
+#pragma unroll
+  for (int hh = 0; hh < VH; ++hh)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r2 = 0; r2 < 4; ++r2) {
+        const int head = 4 * lq + r2;
+        if (head < G) sm_o[w][head][64 * hh + 4 * ln + j] = oacc[hh * 4 + j][r2];
+      }
+  __syncthreads();
+
+  const int nel = G * D;
+  const int64_t out_base = (static_cast<int64_t>(b) * p.Hq + h * G);
+  if (S == 1) {
+    for (int e = tid; e < nel; e += 256) {
+      const int head = e / D;
+      const int dim = e - head * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][head]);
+      float osum = 0.f, lsum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float mw = sm_m[ww][head];
+          const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+          osum += f * sm_o[ww][head][dim];
+          lsum += f * sm_l[ww][head];
+        }
+      }
+      const bool any = lsum > 0.f;
+      p.out[(out_base + head) * D + dim] = f2bf(any ? osum / lsum : 0.f);
+      if (dim == 0 && p.lse != nullptr)
+        p.lse[out_base + head] = any ? (M + fast_log2(lsum)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+
+  const int64_t part = static_cast<int64_t>(pair) * S + split;
+  for (int e = tid; e < nel; e += 256) {
+    const int head = e / D;
+    const int dim = e - head * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][head]);
+    float osum = 0.f, lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float mw = sm_m[ww][head];
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        osum += f * sm_o[ww][head][dim];
+        lsum += f * sm_l[ww][head];
+      }
+    }
+    const bool any = lsum > 0.f;
+    p.part_o[(part * G + head) * D + dim] = any ? osum / lsum : 0.f;
+    if (dim == 0) p.part_lse[part * G + head] = any ? M + fast_log2(lsum) : -INFINITY;
+  }
+
+  // ---- the last split of this (b, h) to finish combines all splits
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const int prev = __hip_atomic_fetch_add(p.counters + pair, 1, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = (prev == S - 1);
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+
+  float* wts = &sm_o[0][0][0];  // S * G <= 128 * 16 floats fit in sm_o
+  const float* plse = p.part_lse + static_cast<int64_t>(pair) * S * G;
+  if (tid < G) {
+    const int head = tid;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, plse[s * G + head]);
+    float tot = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const float ls = plse[s * G + head];
+        const float f = (ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
+        wts[s * G + head] = f;
+        tot += f;
+      }
+    } else {
+      for (int s = 0; s < S; ++s) wts[s * G + head] = 0.f;
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    for (int s = 0; s < S; ++s) wts[s * G + head] *= inv;
+    sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
+  for (int e = tid; e < nel; e += 256) {
+    const int head = e / D;
+    const int dim = e - head * D;
+    float o = 0.f;
+    for (int s = 0; s < S; ++s) o += wts[s * G + head] * po[(s * G + head) * D + dim];
+    p.out[(out_base + head) * D + dim] = f2bf(o);
+    if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
+  }
+  if (tid == 0) __hip_atomic_store(p.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int BS, bool DENSE>
+void launch_one(const DecodeParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE>), dim3(grid), dim3(256), 0, stream, p);
+}
+
+}  // namespace
+
+int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
+  const int64_t pairs = static_cast<int64_t>(d.batch) * d.num_kv_heads;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const int S = a.num_split;
+  DecodeParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.seq_lens = a.seq_lens;
+  p.block_idx = a.block_idx;
+  p.num_selected = a.num_selected;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.sb = d.kv_stride_b;
+  p.sh = d.kv_stride_h;
+  p.st = static_cast<int>(d.kv_stride_t);
+  p.Hq = d.num_q_heads;
+  p.Hkv = d.num_kv_heads;
+  p.G = G;
+  p.Lmax = d.max_seq_len;
+  p.max_sel = a.max_selected;
+  p.num_split = S;
+  p.scale_log2 = a.scale * kLog2e;
+  if (S > 1) {
+    char* ws = static_cast<char*>(a.workspace);
+    size_t cbytes = static_cast<size_t>(pairs) * sizeof(int32_t);
+    cbytes = (cbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
+    size_t lbytes = static_cast<size_t>(pairs) * S * G * sizeof(float);
+    lbytes = (lbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
+    p.counters = reinterpret_cast<int32_t*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + cbytes);
+    p.part_o = reinterpret_cast<float*>(ws + cbytes + lbytes);
+  }
+  const int64_t grid64 = pairs * S;
+  if (grid64 > 0x7fffffff) {
+    set_error("decode grid too large");
+    return SEER_ERR_UNSUPPORTED;
+  }
+  const int grid = static_cast<int>(grid64);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool dense = (a.block_idx == nullptr);
+  const int key = (d.head_dim == 128 ? 4 : 0) | (d.block_size == 128 ? 2 : 0) | (dense ? 1 : 0);
+  switch (key) {
+    case 0: launch_one<64, 64, false>(p, grid, s); break;
+    case 1: launch_one<64, 64, true>(p, grid, s); break;
+    case 2: launch_one<64, 128, false>(p, grid, s); break;
+    case 3: launch_one<64, 128, true>(p, grid, s); break;
+    case 4: launch_one<128, 64, false>(p, grid, s); break;
+    case 5: launch_one<128, 64, true>(p, grid, s); break;
+    case 6: launch_one<128, 128, false>(p, grid, s); break;
+    default: launch_one<128, 128, true>(p, grid, s); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error(std::string("decode launch: ") + hipGetErrorString(e));
+    return SEER_ERR_HIP;
+  }
+  return SEER_OK;
+}
+
+}  // namespace seer

@@ -1,0 +1,198 @@
+// The extern "C" entry points of libseer: argument checks, then launches.
+// No HIP call happens before every host-side check has passed.
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+
+#include "seer_internal.h"
+
+using seer::check_dims;
+using seer::check_ptr;
+
+namespace {
+
+int fail(int code, const std::string& why) {
+  seer::set_error(why);
+  return code;
+}
+
+// Runs a check that fills `why`; records it on failure.
+#define SEER_CHECK(call)                     \
+  do {                                       \
+    std::string why_;                        \
+    int rc_ = call;                          \
+    if (rc_ != SEER_OK) return fail(rc_, why_); \
+  } while (0)
+
+int resolve_split(const seer_dims* d, int max_blocks, int num_split, int* out) {
+  if (num_split < 0 || num_split > seer::kMaxSplit)
+    return fail(SEER_ERR_INVALID_ARG, "num_split must be in [0, 128]");
+  if (num_split > 0) {
+    *out = num_split;
+    return SEER_OK;
+  }
+  int cus = 0;
+  int rc = seer::device_cu_count(&cus);
+  if (rc != SEER_OK) return rc;
+  *out = seer::auto_num_split(d, max_blocks, cus);
+  return SEER_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int seer_kcomp_update(const seer_dims* dims, const uint16_t* k_nope, const uint16_t* w_k,
+                      const int32_t* seq_lens, int32_t* kcomp_lens, uint16_t* kcomp,
+                      int32_t max_new_blocks, double rope_theta, void* stream) {
+  SEER_CHECK(check_dims(dims, &why_));
+  SEER_CHECK(check_ptr(k_nope, 16, "k_nope", &why_));
+  SEER_CHECK(check_ptr(w_k, 16, "w_k", &why_));
+  SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
+  SEER_CHECK(check_ptr(kcomp_lens, 4, "kcomp_lens", &why_));
+  SEER_CHECK(check_ptr(kcomp, 16, "kcomp", &why_));
+  if (max_new_blocks < 1) return fail(SEER_ERR_INVALID_ARG, "max_new_blocks must be >= 1");
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(SEER_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+  if (max_new_blocks > seer::nb_max(dims)) max_new_blocks = static_cast<int32_t>(seer::nb_max(dims));
+  seer::KcompArgs a{k_nope, w_k, seq_lens, kcomp_lens, kcomp, max_new_blocks, rope_theta};
+  return seer::launch_kcomp(*dims, a, stream);
+}
+
+size_t seer_gate_workspace_bytes(const seer_dims* dims) {
+  std::string why;
+  if (check_dims(dims, &why) != SEER_OK) return 0;
+  return seer::gate_workspace_bytes(dims);
+}
+
+int seer_gate_scores(const seer_dims* dims, const uint16_t* q_nope, const uint16_t* w_q,
+                     const uint16_t* kcomp, const int32_t* kcomp_lens, const int32_t* seq_lens,
+                     double rope_theta, void* workspace, size_t workspace_bytes, float* logits,
+                     void* stream) {
+  SEER_CHECK(check_dims(dims, &why_));
+  SEER_CHECK(check_ptr(q_nope, 16, "q_nope", &why_));
+  SEER_CHECK(check_ptr(w_q, 16, "w_q", &why_));
+  SEER_CHECK(check_ptr(kcomp, 16, "kcomp", &why_));
+  SEER_CHECK(check_ptr(kcomp_lens, 4, "kcomp_lens", &why_));
+  SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
+  SEER_CHECK(check_ptr(logits, 4, "logits", &why_));
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(SEER_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+  if (workspace == nullptr || workspace_bytes < seer::gate_workspace_bytes(dims))
+    return fail(SEER_ERR_WORKSPACE, "gate workspace missing or smaller than seer_gate_workspace_bytes()");
+  SEER_CHECK(check_ptr(workspace, 16, "workspace", &why_));
+  seer::GateArgs a{q_nope, w_q, kcomp, kcomp_lens, seq_lens, rope_theta,
+                   static_cast<float*>(workspace), logits};
+  return seer::launch_gate(*dims, a, stream);
+}
+
+int seer_select_blocks(const seer_dims* dims, const float* logits, const int32_t* kcomp_lens,
+                       const int32_t* seq_lens, int32_t mode, int32_t topk_blocks, float threshold,
+                       int32_t max_selected, int32_t* block_idx, int32_t* num_selected,
+                       void* stream) {
+  SEER_CHECK(check_dims(dims, &why_));
+  SEER_CHECK(check_ptr(logits, 4, "logits", &why_));
+  SEER_CHECK(check_ptr(kcomp_lens, 4, "kcomp_lens", &why_));
+  SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
+  SEER_CHECK(check_ptr(block_idx, 4, "block_idx", &why_));
+  SEER_CHECK(check_ptr(num_selected, 4, "num_selected", &why_));
+  const int64_t nbm = seer::nb_max(dims);
+  if (nbm > seer::kMaxNBSelect)
+    return fail(SEER_ERR_UNSUPPORTED, "select needs ceil(max_seq_len / block_size) <= 8192");
+  if (mode == SEER_SELECT_TOPK) {
+    if (topk_blocks < 0) return fail(SEER_ERR_INVALID_ARG, "topk_blocks must be >= 0");
+    const int64_t need = std::min<int64_t>(static_cast<int64_t>(topk_blocks) + 1, nbm);
+    if (max_selected < need)
+      return fail(SEER_ERR_INVALID_ARG, "max_selected must be >= min(topk_blocks + 1, NBmax)");
+  } else if (mode == SEER_SELECT_THRESHOLD) {
+    if (!(threshold >= 0.0f && threshold <= 1.0f))
+      return fail(SEER_ERR_INVALID_ARG, "threshold must be in [0, 1]");
+    if (max_selected < nbm)
+      return fail(SEER_ERR_INVALID_ARG, "threshold mode needs max_selected >= NBmax");
+  } else {
+    return fail(SEER_ERR_INVALID_ARG, "mode must be SEER_SELECT_TOPK or SEER_SELECT_THRESHOLD");
+  }
+  if (max_selected < 1 || max_selected > nbm)
+    return fail(SEER_ERR_INVALID_ARG, "max_selected must be in [1, NBmax]");
+  seer::SelectArgs a{logits, kcomp_lens, seq_lens, mode, topk_blocks, threshold,
+                     max_selected, block_idx, num_selected};
+  return seer::launch_select(*dims, a, stream);
+}
+
+size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks, int32_t num_split) {
+  std::string why;
+  if (check_dims(dims, &why) != SEER_OK || max_blocks < 1) return 0;
+  int s = 0;
+  if (resolve_split(dims, max_blocks, num_split, &s) != SEER_OK) return 0;
+  const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
+  return seer::decode_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
+                                      dims->head_dim);
+}
+
+int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks, int32_t num_split,
+                          int32_t* num_split_out) {
+  SEER_CHECK(check_dims(dims, &why_));
+  if (num_split_out == nullptr) return fail(SEER_ERR_INVALID_ARG, "num_split_out is NULL");
+  if (max_blocks < 1) return fail(SEER_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  int s = 0;
+  int rc = resolve_split(dims, max_blocks, num_split, &s);
+  if (rc != SEER_OK) return rc;
+  *num_split_out = s;
+  return SEER_OK;
+}
+
+static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const int32_t* seq_lens, const int32_t* block_idx,
+                         const int32_t* num_selected, int32_t max_blocks, float scale,
+                         int32_t num_split, void* workspace, size_t workspace_bytes,
+                         uint16_t* out, float* lse, void* stream) {
+  SEER_CHECK(check_dims(dims, &why_));
+  SEER_CHECK(check_ptr(q, 16, "q", &why_));
+  SEER_CHECK(check_ptr(k, 16, "k_cache", &why_));
+  SEER_CHECK(check_ptr(v, 16, "v_cache", &why_));
+  SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
+  SEER_CHECK(check_ptr(out, 16, "out", &why_));
+  if (lse != nullptr) SEER_CHECK(check_ptr(lse, 4, "lse", &why_));
+  if (!std::isfinite(scale)) return fail(SEER_ERR_INVALID_ARG, "scale must be finite");
+  if (max_blocks < 1 || max_blocks > seer::nb_max(dims))
+    return fail(SEER_ERR_INVALID_ARG, "max_selected must be in [1, NBmax]");
+  int s = 0;
+  int rc = resolve_split(dims, max_blocks, num_split, &s);
+  if (rc != SEER_OK) return rc;
+  const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
+  const size_t need = seer::decode_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
+                                                   dims->head_dim);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SEER_ERR_WORKSPACE, "decode workspace missing or smaller than seer_decode_workspace_bytes()");
+    SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
+  }
+  seer::DecodeArgs a{q, k, v, seq_lens, block_idx, num_selected, max_blocks, scale, s,
+                     workspace, out, lse};
+  return seer::launch_decode(*dims, a, stream);
+}
+
+int seer_sparse_decode(const seer_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                       const uint16_t* v_cache, const int32_t* seq_lens, const int32_t* block_idx,
+                       const int32_t* num_selected, int32_t max_selected, float scale,
+                       int32_t num_split, void* workspace, size_t workspace_bytes, uint16_t* out,
+                       float* lse, void* stream) {
+  SEER_CHECK(check_ptr(block_idx, 4, "block_idx", &why_));
+  SEER_CHECK(check_ptr(num_selected, 4, "num_selected", &why_));
+  return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,
+                       scale, num_split, workspace, workspace_bytes, out, lse, stream);
+}
+
+int seer_dense_decode(const seer_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                      const uint16_t* v_cache, const int32_t* seq_lens, float scale,
+                      int32_t num_split, void* workspace, size_t workspace_bytes, uint16_t* out,
+                      float* lse, void* stream) {
+  std::string why;
+  if (check_dims(dims, &why) != SEER_OK) return fail(check_dims(dims, &why), why);
+  return decode_common(dims, q, k_cache, v_cache, seq_lens, nullptr, nullptr,
+                       static_cast<int32_t>(seer::nb_max(dims)), scale, num_split, workspace,
+                       workspace_bytes, out, lse, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal interfaces between the C ABI layer, the HIP-free argument checks
+// and the kernel launchers.  Not installed; not part of the ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/seer.h"
+
+namespace seer {
+
+// ----------------------------------------------------------------- limits
+constexpr int kMaxGroup = 16;          // query heads per KV head (MFMA N = 16)
+constexpr int kMaxNBSelect = 8192;     // blocks per sequence the select kernel holds in LDS
+constexpr int kMaxSplit = 128;         // splits per (b, h) in the decode kernel
+constexpr int kCounterBytes = 256;     // alignment of the partials after the counters
+
+// ------------------------------------------------------- argument checks
+// These live in a HIP-free translation unit so that a CPU-only test can
+// exercise every error path.  Each returns SEER_OK or an error code and
+// fills *why.
+int check_dims(const seer_dims* d, std::string* why);
+int check_kv(const seer_dims* d, const void* k, const char* name, std::string* why);
+int check_ptr(const void* p, size_t align, const char* name, std::string* why);
+
+int64_t nb_max(const seer_dims* d);  // ceil(Lmax / b)
+size_t gate_workspace_bytes(const seer_dims* d);
+// Workspace of the decode kernel for `pairs` (b, h) pairs, `num_split`
+// splits and group size g.
+size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim);
+// Automatic split count given the device's compute-unit count.
+int auto_num_split(const seer_dims* d, int max_blocks, int num_cus);
+
+void set_error(const std::string& msg);
+const char* last_error();
+
+// ------------------------------------------------------ kernel launchers
+// Implemented in the .hip files.  Arguments were validated by the caller.
+struct KcompArgs {
+  const uint16_t* k_nope;
+  const uint16_t* w_k;
+  const int32_t* seq_lens;
+  int32_t* kcomp_lens;
+  uint16_t* kcomp;
+  int max_new_blocks;
+  double theta;
+};
+int launch_kcomp(const seer_dims& d, const KcompArgs& a, void* stream);
+
+struct GateArgs {
+  const uint16_t* q_nope;
+  const uint16_t* w_q;
+  const uint16_t* kcomp;
+  const int32_t* kcomp_lens;
+  const int32_t* seq_lens;
+  double theta;
+  float* q_gate;   // workspace [B, H_kv, d_gate]
+  float* logits;
+};
+int launch_gate(const seer_dims& d, const GateArgs& a, void* stream);
+
+struct SelectArgs {
+  const float* logits;
+  const int32_t* kcomp_lens;
+  const int32_t* seq_lens;
+  int mode;
+  int topk;
+  float tau;
+  int max_selected;
+  int32_t* block_idx;
+  int32_t* num_selected;
+};
+int launch_select(const seer_dims& d, const SelectArgs& a, void* stream);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq_lens;
+  const int32_t* block_idx;     // nullptr = dense
+  const int32_t* num_selected;  // nullptr = dense
+  int max_selected;             // index row length (sparse)
+  float scale;
+  int num_split;
+  void* workspace;
+  uint16_t* out;
+  float* lse;
+};
+int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
+
+// Device query (HIP): compute units of the current device, cached.
+int device_cu_count(int* out);
+
+}  // namespace seer

@@ -1,0 +1,246 @@
+/*
+ * seer.h -- C ABI of libseer, the MI355X (gfx950) decode-time hot path of
+ * SeerAttention-R block-sparse attention.
+ *
+ * Pages cited:
+ *   [CP] chapterpal.com summary page "SeerAttention-R: Sparse Attention
+ *        Adaptation for Long Reasoning" (its numbered "Knowl" sections);
+ *   [PN] papernotes.org ICLR 2026 notes page "Sparse Attention Adaptation
+ *        for Long Reasoning" (its "key design" paragraphs).
+ *
+ * One decode step of one attention layer is
+ *   seer_kcomp_update  -> seer_gate_scores -> seer_select_blocks
+ *   -> seer_sparse_decode            (seer_dense_decode is the full baseline)
+ *
+ * Conventions shared by every call
+ *   - "bf16" buffers hold raw bfloat16 bit patterns (uint16_t).
+ *   - Every pointer argument is a DEVICE pointer unless marked (host); the
+ *     `dims` struct is always a host pointer.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and returns as soon as its kernels are
+ *     queued.  No call synchronises the host with the device.
+ *   - The caller owns every buffer.  The library allocates nothing and keeps
+ *     no pointer after a call returns.  Outputs are fully overwritten
+ *     (including padding), so callers never pre-initialise them; the only
+ *     exception is the decode workspace, which must be zero-filled once
+ *     before its first use (see seer_decode_workspace_bytes).
+ *   - Host-detectable errors return before anything is launched; nothing is
+ *     written.  A kernel launch failure returns SEER_ERR_HIP.  Device-side
+ *     data problems cannot be reported synchronously: out-of-range lengths
+ *     are clamped to [0, max_seq_len], block indices outside
+ *     [0, ceil(L/b)) are skipped, and stale cache counters are clamped.
+ *   - seer_last_error_message() gives a human-readable reason for the most
+ *     recent non-OK return on the calling thread.
+ *
+ * Tensor layouts (row-major, innermost last)
+ *   q, q_nope  [B, H_q, d]            bf16, contiguous.  Query head
+ *                                     hq = h*g + i belongs to KV head h
+ *                                     (g = H_q / H_kv).
+ *   K, V, K_nope [B, H_kv, Lmax, d]   bf16; element strides kv_stride_b,
+ *                                     kv_stride_h, kv_stride_t, d contiguous.
+ *                                     Token t of sequence b sits at
+ *                                     b*sb + h*sh + t*st.  K is post-RoPE (the
+ *                                     model's), K_nope pre-RoPE.
+ *   w_q        [H_kv, d_gate, g*d]    bf16, contiguous (one W_q per KV head,
+ *                                     [PN key design 1]).
+ *   w_k        [H_kv, d_gate, 3*d]    bf16, contiguous; column blocks are
+ *                                     [max | min | avg] ([CP Knowl 1]).
+ *   kcomp      [B, H_kv, NBmax, d_gate] bf16, contiguous;
+ *                                     NBmax = ceil(Lmax / b).
+ *   seq_lens, kcomp_lens  [B]         int32.  seq_lens counts the current
+ *                                     token.
+ *   logits     [B, H_kv, NBmax]       float32, un-softmaxed block scores.
+ *   block_idx  [B, H_kv, max_selected] int32, ascending, -1 padded.
+ *   num_selected [B, H_kv]            int32.
+ *   out        [B, H_q, d]            bf16.
+ *   lse        [B, H_q]               float32 natural-log sum of exp.
+ */
+#ifndef SEER_H_
+#define SEER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SEER_OK = 0,
+  SEER_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value   */
+  SEER_ERR_UNSUPPORTED = 2, /* valid but not built: d, d_gate, b, g, NBmax  */
+  SEER_ERR_WORKSPACE = 3,   /* workspace missing or too small               */
+  SEER_ERR_HIP = 4          /* HIP runtime error (launch, device query)     */
+};
+
+enum { SEER_SELECT_TOPK = 1, SEER_SELECT_THRESHOLD = 2 };
+
+typedef struct seer_dims {
+  int32_t batch;        /* B >= 1                                           */
+  int32_t num_q_heads;  /* H_q, a multiple of H_kv                          */
+  int32_t num_kv_heads; /* H_kv >= 1; g = H_q / H_kv must be in [1, 16]      */
+  int32_t head_dim;     /* d: 64 or 128                                     */
+  int32_t d_gate;       /* gate width per KV head: 64 or 128                */
+  int32_t block_size;   /* b: 64 or 128                                     */
+  int32_t max_seq_len;  /* Lmax: KV capacity per sequence (tokens)          */
+  int32_t reserved;     /* must be 0                                        */
+  int64_t kv_stride_b;  /* element strides of K, V and K_nope, multiples of */
+  int64_t kv_stride_h;  /* 8 (16-byte rows); kv_stride_t >= d               */
+  int64_t kv_stride_t;
+} seer_dims;
+
+/*
+ * seer_kcomp_update -- append K Compression Cache entries for blocks that
+ * have become complete.
+ *
+ * [CP Knowl 5]: the cache holds K_gate per block and is updated once every b
+ * new tokens by pooling the latest b keys and applying the linear layer.
+ * [CP Knowl 2]: K_gate = RoPE(W_k concat[P_max, P_min, P_avg](K_nope)) with
+ * kernel = stride = b pooling; [CP Knowl 1]: the RoPE position of a
+ * compressed block is its first token.
+ *
+ * For every sequence b and KV head h, with L = seq_lens[b], nb = floor(L/b)
+ * and c = kcomp_lens[b], entries j = c .. min(nb, c + max_new_blocks) - 1 are
+ * computed as bf16(RoPE(W_k[h] . [max, min, mean of K_nope rows j*b ..
+ * j*b+b-1], j*b)) (round to nearest even), and kcomp_lens[b] is then raised
+ * to min(nb, c + max_new_blocks).  Entries already present are not touched.
+ * Bulk build of a prompt: kcomp_lens = 0, max_new_blocks = NBmax.
+ * Decode: max_new_blocks = 1, once per step, before seer_gate_scores.
+ *
+ *   k_nope      pre-RoPE keys (layout above); may alias k_cache.
+ *   w_k         [H_kv, d_gate, 3d] bf16.
+ *   seq_lens    [B] int32 (read).   kcomp_lens [B] int32 (read, then raised).
+ *   kcomp       [B, H_kv, NBmax, d_gate] bf16 (entries written).
+ *   max_new_blocks >= 1; rope_theta > 0 (RoPE base, e.g. 10000).
+ * Launches two kernels; the second raises kcomp_lens after all entries are
+ * written.
+ */
+int seer_kcomp_update(const seer_dims* dims, const uint16_t* k_nope,
+                      const uint16_t* w_k, const int32_t* seq_lens,
+                      int32_t* kcomp_lens, uint16_t* kcomp,
+                      int32_t max_new_blocks, double rope_theta, void* stream);
+
+/*
+ * seer_gate_scores -- block scores of the current token against the cache.
+ *
+ * [CP Knowl 2]: Q_gate = RoPE(W_q reshape(Q_nope, [.., g*d])) and the scores
+ * are Q_gate K_gate^T / sqrt(d_gate) (softmax not applied: [CP Knowl 5] top-k
+ * runs on the un-softmaxed logits).  The query position is L-1.
+ *
+ * Writes logits[b, h, j] = Q_gate[b,h] . kcomp[b,h,j] / sqrt(d_gate) for
+ * j < n_c = min(kcomp_lens[b], floor(L/b)), and -inf for n_c <= j < NBmax.
+ * Q_gate itself ([B, H_kv, d_gate] float32) is left at the start of the
+ * workspace.
+ *
+ *   q_nope     [B, H_q, d] bf16.   w_q [H_kv, d_gate, g*d] bf16.
+ *   workspace  >= seer_gate_workspace_bytes(dims) bytes, 16-byte aligned,
+ *              no initialisation needed.
+ *   logits     [B, H_kv, NBmax] float32.
+ */
+size_t seer_gate_workspace_bytes(const seer_dims* dims);
+int seer_gate_scores(const seer_dims* dims, const uint16_t* q_nope,
+                     const uint16_t* w_q, const uint16_t* kcomp,
+                     const int32_t* kcomp_lens, const int32_t* seq_lens,
+                     double rope_theta, void* workspace, size_t workspace_bytes,
+                     float* logits, void* stream);
+
+/*
+ * seer_select_blocks -- binarise block scores into active-block indices.
+ *
+ * [CP Knowl 5]: (1) token budget: top-k block indices by un-softmaxed logit,
+ * k = ceil(budget / b) (the caller passes k); (2) threshold: blocks whose
+ * softmax score exceeds tau.  The incomplete last block is selected
+ * unconditionally.  [CP Knowl 6]: the index tensor is
+ * [batch, heads_kv, max_selected_blocks].
+ *
+ * With n_c = min(kcomp_lens[b], floor(L/b)) scored blocks and
+ * N = ceil(L/b) blocks in all:
+ *   TOPK:      the min(k, n_c) largest logits; equal logits go to the lower
+ *              index.
+ *   THRESHOLD: the j < n_c with logits[j] > ln(tau) + logsumexp(logits[0..n_c))
+ *              (softmax_j > tau, strict), evaluated in float32.
+ * plus every block in [n_c, N) (normally only the partial block).  Indices
+ * are written ascending, -1 after the last; num_selected gets the count.
+ * If more than max_selected blocks qualify (only when the cache lags), the
+ * lowest max_selected are kept.
+ *
+ *   mode            SEER_SELECT_TOPK (uses topk_blocks >= 0) or
+ *                   SEER_SELECT_THRESHOLD (uses 0 <= threshold <= 1).
+ *   max_selected    capacity per (b, h): TOPK needs
+ *                   >= min(topk_blocks + 1, NBmax), THRESHOLD needs >= NBmax.
+ *   NBmax <= 8192 (SEER_ERR_UNSUPPORTED otherwise).
+ */
+int seer_select_blocks(const seer_dims* dims, const float* logits,
+                       const int32_t* kcomp_lens, const int32_t* seq_lens,
+                       int32_t mode, int32_t topk_blocks, float threshold,
+                       int32_t max_selected, int32_t* block_idx,
+                       int32_t* num_selected, void* stream);
+
+/*
+ * Decode workspace: split partials plus one completion counter per
+ * (b, h).  `max_blocks` is max_selected (sparse) or NBmax (dense);
+ * `num_split` 0 means "choose automatically" (queries the current device).
+ * The counters must be ZERO before the first call that uses a workspace;
+ * every call leaves them zero again, so one zero-fill at allocation is
+ * enough.  One workspace must not be used by two calls that can run at the
+ * same time.
+ */
+size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks,
+                                   int32_t num_split);
+
+/* The split count a decode call will use (resolves num_split = 0). */
+int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks,
+                          int32_t num_split, int32_t* num_split_out /* host */);
+
+/*
+ * seer_sparse_decode -- block-sparse flash decoding over the active blocks.
+ *
+ * [CP Knowl 6]: grid (batch, heads_kv, num_split); the work of each
+ * (b, h) is split along num_split from its list of active blocks, the kernel
+ * loops only over active indices and skips invalid entries; [PN key design
+ * 4] same.  Split results are merged by log-sum-exp in the same launch.
+ *
+ * For each query head hq = h*g + i of sequence b: over the tokens
+ * T = union over the first num_selected[b,h] entries j of block_idx[b,h] with
+ * 0 <= j < ceil(L/b) of [j*b, min(j*b+b, L)),
+ *   out[b,hq] = sum_t softmax_T(scale * q.K_t) V_t   (bf16, round to nearest)
+ *   lse[b,hq] = ln sum_T exp(scale * q.K_t)          (float32; may be NULL)
+ * An empty T gives out = 0 and lse = -inf.
+ *
+ *   q          [B, H_q, d] post-RoPE bf16.   k_cache, v_cache: layout above.
+ *   block_idx  [B, H_kv, max_selected], num_selected [B, H_kv] (as written
+ *              by seer_select_blocks; indices must not repeat).
+ *   scale      usually 1/sqrt(d).   num_split 0 = automatic.
+ *   workspace  >= seer_decode_workspace_bytes(dims, max_selected, num_split)
+ *              bytes, 256-byte aligned, counters zero (see above).
+ */
+int seer_sparse_decode(const seer_dims* dims, const uint16_t* q,
+                       const uint16_t* k_cache, const uint16_t* v_cache,
+                       const int32_t* seq_lens, const int32_t* block_idx,
+                       const int32_t* num_selected, int32_t max_selected,
+                       float scale, int32_t num_split, void* workspace,
+                       size_t workspace_bytes, uint16_t* out, float* lse,
+                       void* stream);
+
+/*
+ * seer_dense_decode -- the full-attention decode baseline: the same kernel
+ * over every block 0 .. ceil(L/b)-1 (the role FlashAttention-3 plays in
+ * [CP Knowl 9]).  Arguments as seer_sparse_decode; the workspace is sized
+ * with max_blocks = NBmax.
+ */
+int seer_dense_decode(const seer_dims* dims, const uint16_t* q,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const int32_t* seq_lens, float scale, int32_t num_split,
+                      void* workspace, size_t workspace_bytes, uint16_t* out,
+                      float* lse, void* stream);
+
+/* Host-only helpers. */
+const char* seer_status_string(int status);
+const char* seer_last_error_message(void);
+const char* seer_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEER_H_ */

@@ -1,0 +1,482 @@
+"""GPU parity of the HIP decode path against the float64 oracle.
+
+Every test calls the library through its C ABI (ctypes binding) on seeded
+synthetic inputs and compares with the oracle element by element, stage by
+stage (each kernel fed identical inputs) and end to end.  Tolerances are in
+tests/seer_testlib.py.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from seer_testlib import (assert_lse_close, assert_out_close, bf16_ulp, check_topk_set, f64,
+                          host_inputs, oracle_chain, threshold_value)
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_seer_amd as S
+    S.lib()  # raises if the library is not built
+    return S
+
+
+def make_kv(B, Hkv, lmax, d, gen, poison_from=None):
+    k = torch.randn((B, Hkv, lmax, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, lmax, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    if poison_from is not None:  # never-read slots hold NaN
+        for b, L in enumerate(poison_from):
+            k[b, :, L:] = float("nan")
+            v[b, :, L:] = float("nan")
+    return k, v
+
+
+# ----------------------------------------------------------- sparse decode
+
+DECODE_CASES = [
+    # d, bs, Hq, Hkv, lens
+    (64, 64, 4, 1, [1024]),
+    (128, 64, 32, 8, [1000, 1]),
+    (128, 64, 40, 8, [4096, 700]),
+    (128, 128, 32, 8, [2000, 129]),
+    (64, 128, 8, 8, [300, 63]),
+    (128, 64, 16, 1, [5000]),
+    (64, 64, 2, 2, [64, 65]),
+]
+
+
+@pytest.mark.parametrize("d,bs,Hq,Hkv,lens", DECODE_CASES)
+@pytest.mark.parametrize("num_split", [1, 3, 0])
+def test_sparse_decode_matches_oracle(S, d, bs, Hq, Hkv, lens, num_split):
+    say(f"sparse_decode d={d} bs={bs} Hq={Hq} Hkv={Hkv} lens={lens} split={num_split}")
+    B = len(lens)
+    g = Hq // Hkv
+    lmax = max(lens) + 37
+    gen = torch.Generator().manual_seed(7 + d + bs + Hq)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    k, v = make_kv(B, Hkv, lmax, d, gen, poison_from=lens)
+    nbm = -(-lmax // bs)
+    max_sel = nbm
+    rng = np.random.default_rng(11)
+    idx = np.full((B, Hkv, max_sel), -1, dtype=np.int32)
+    nsel = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        total = -(-lens[b] // bs)
+        for h in range(Hkv):
+            n = int(rng.integers(0, total + 1))
+            chosen = sorted(rng.choice(total, size=n, replace=False).tolist()) if n else []
+            if chosen and len(chosen) + 2 <= max_sel and rng.random() < 0.5:
+                chosen = chosen + [-1, total + 3]  # invalid entries inside the count
+            idx[b, h, :len(chosen)] = chosen
+            nsel[b, h] = len(chosen)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    nsel_d = torch.from_numpy(nsel).to(DEV)
+    ns = S.seer_decode_num_split(dims, max_sel, num_split)
+    ws = torch.zeros(max(S.seer_decode_workspace_bytes(dims, max_sel, ns), 4) // 4 + 64,
+                     dtype=torch.float32, device=DEV)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    S.seer_sparse_decode(dims, qd, kd, vd, seq, idx_d, nsel_d, max_sel, scale, ns, ws, out, lse)
+    torch.cuda.synchronize()
+    og, lg = f64(out), f64(lse)
+    for b in range(B):
+        for h in range(Hkv):
+            qq = f64(q[b, h * g:(h + 1) * g])
+            kk, vv = f64(k[b, h, :lens[b]]), f64(v[b, h, :lens[b]])
+            blocks = idx[b, h, :nsel[b, h]].tolist()
+            o_ref, l_ref = O.sparse_decode_pair(qq, kk, vv, lens[b], blocks, bs, scale)
+            assert_out_close(og[b, h * g:(h + 1) * g], o_ref, f"b={b} h={h}")
+            assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, f"b={b} h={h}")
+    # the counters in the workspace are left at zero
+    if ns > 1:
+        assert int(ws[: B * Hkv].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("d,bs,Hq,Hkv,lens", DECODE_CASES)
+def test_dense_decode_matches_oracle(S, d, bs, Hq, Hkv, lens):
+    say(f"dense_decode d={d} bs={bs} Hq={Hq} Hkv={Hkv} lens={lens}")
+    B = len(lens)
+    g = Hq // Hkv
+    lmax = max(lens) + 5
+    gen = torch.Generator().manual_seed(3 + d + bs)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    k, v = make_kv(B, Hkv, lmax, d, gen, poison_from=lens)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    ns = S.seer_decode_num_split(dims, dims.nb_max, 0)
+    ws = torch.zeros(max(S.seer_decode_workspace_bytes(dims, dims.nb_max, ns), 4) // 4 + 64,
+                     dtype=torch.float32, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    S.seer_dense_decode(dims, q.to(DEV), k.to(DEV), v.to(DEV),
+                        torch.tensor(lens, dtype=torch.int32, device=DEV), scale, ns, ws, out, lse)
+    torch.cuda.synchronize()
+    og, lg = f64(out), f64(lse)
+    for b in range(B):
+        for h in range(Hkv):
+            qq = f64(q[b, h * g:(h + 1) * g])
+            o_ref, l_ref = O.dense_decode_pair(qq, f64(k[b, h, :lens[b]]), f64(v[b, h, :lens[b]]),
+                                               lens[b], scale)
+            assert_out_close(og[b, h * g:(h + 1) * g], o_ref, f"b={b} h={h}")
+            assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, f"b={b} h={h}")
+
+
+def test_decode_empty_selection_and_zero_length(S):
+    say("decode empty selection / zero length")
+    B, Hq, Hkv, d, bs, lmax = 2, 8, 2, 128, 64, 256
+    gen = torch.Generator().manual_seed(5)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16).to(DEV)
+    k, v = make_kv(B, Hkv, lmax, d, gen)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    seq = torch.tensor([200, 0], dtype=torch.int32, device=DEV)
+    idx = torch.full((B, Hkv, 4), -1, dtype=torch.int32, device=DEV)
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device=DEV)
+    for ns in (1, 2):
+        ws = torch.zeros(S.seer_decode_workspace_bytes(dims, 4, ns) // 4 + 64, dtype=torch.float32,
+                         device=DEV)
+        out = torch.full((B, Hq, d), 7.0, dtype=torch.bfloat16, device=DEV)
+        lse = torch.zeros((B, Hq), dtype=torch.float32, device=DEV)
+        S.seer_sparse_decode(dims, q, k.to(DEV), v.to(DEV), seq, idx, nsel, 4, 0.1, ns, ws, out, lse)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)
+        assert torch.all(torch.isneginf(lse))
+    # dense with L = 0 for sequence 1
+    ws = torch.zeros(S.seer_decode_workspace_bytes(dims, dims.nb_max, 2) // 4 + 64,
+                     dtype=torch.float32, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    S.seer_dense_decode(dims, q, k.to(DEV), v.to(DEV), seq, 0.1, 2, ws, out, lse)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    assert torch.all(torch.isfinite(lse[0]))
+
+
+def test_decode_is_deterministic(S):
+    say("decode determinism")
+    B, Hq, Hkv, d, bs, L = 4, 40, 8, 128, 64, 4096
+    gen = torch.Generator().manual_seed(9)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16).to(DEV)
+    k, v = make_kv(B, Hkv, L, d, gen)
+    k, v = k.to(DEV), v.to(DEV)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, L)
+    seq = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    outs = []
+    for _ in range(2):
+        ws = torch.zeros(S.seer_decode_workspace_bytes(dims, dims.nb_max, 8) // 4 + 64,
+                         dtype=torch.float32, device=DEV)
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+        S.seer_dense_decode(dims, q, k, v, seq, 0.088, 8, ws, out, lse)
+        outs.append((out.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_decode_strided_kv_layout(S):
+    say("decode strided KV [B, L, H, d]")
+    B, Hq, Hkv, d, bs, L = 2, 8, 2, 128, 64, 700
+    gen = torch.Generator().manual_seed(21)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    kbl = torch.randn((B, L, Hkv, d), generator=gen).to(torch.bfloat16)
+    vbl = torch.randn((B, L, Hkv, d), generator=gen).to(torch.bfloat16)
+    kd = kbl.to(DEV).permute(0, 2, 1, 3)  # [B, H, L, d] view with token stride H*d
+    vd = vbl.to(DEV).permute(0, 2, 1, 3)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, L, kv_strides=kd.stride()[:3])
+    seq = torch.tensor([L, 333], dtype=torch.int32, device=DEV)
+    ws = torch.zeros(S.seer_decode_workspace_bytes(dims, dims.nb_max, 2) // 4 + 64,
+                     dtype=torch.float32, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    S.seer_dense_decode(dims, q.to(DEV), kd, vd, seq, 0.088, 2, ws, out, None)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for b, Lb in enumerate([L, 333]):
+        for h in range(Hkv):
+            o_ref, _ = O.dense_decode_pair(f64(q[b, h * g:(h + 1) * g]), f64(kbl[b, :Lb, h]),
+                                           f64(vbl[b, :Lb, h]), Lb, 0.088)
+            assert_out_close(f64(out[b, h * g:(h + 1) * g]), o_ref, f"b={b} h={h}")
+
+
+# ------------------------------------------------------ compression cache
+
+@pytest.mark.parametrize("d,dg,bs,lens", [(64, 64, 64, [1024, 70]), (128, 128, 64, [4100, 64]),
+                                          (128, 64, 128, [1000, 300]), (64, 128, 128, [129, 5])])
+def test_kcomp_bulk_and_incremental_match_oracle(S, d, dg, bs, lens):
+    say(f"kcomp d={d} dg={dg} bs={bs} lens={lens}")
+    B, Hq, Hkv = len(lens), 8, 2
+    lmax = max(lens) + 3
+    gen = torch.Generator().manual_seed(31 + d + dg)
+    k, _ = make_kv(B, Hkv, lmax, d, gen)
+    wk = (torch.randn((Hkv, dg, 3 * d), generator=gen) / math.sqrt(3 * d)).to(torch.bfloat16)
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, lmax)
+    kd, wkd = k.to(DEV), wk.to(DEV)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kc = torch.full((B, Hkv, dims.nb_max, dg), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kl = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    S.seer_kcomp_update(dims, kd, wkd, seq, kl, kc, dims.nb_max, 10000.0)
+    torch.cuda.synchronize()
+    assert kl.cpu().tolist() == [L // bs for L in lens]
+    gpu = f64(kc)
+    worst = 0
+    n_off = 0
+    n_tot = 0
+    for b in range(B):
+        for h in range(Hkv):
+            ref = O.build_kcomp(f64(k[b, h]), f64(wk[h]), lens[b], bs)
+            got = gpu[b, h, :lens[b] // bs]
+            diff = np.abs(got - ref)
+            ulp = bf16_ulp(ref)
+            assert np.all(diff <= ulp * 1.0001), f"kcomp b={b} h={h} beyond one bf16 step"
+            n_off += int((diff > 0).sum())
+            n_tot += diff.size
+            worst = max(worst, float((diff / ulp).max()) if diff.size else 0.0)
+    assert n_off <= max(2, n_tot // 500), f"{n_off} of {n_tot} entries off by one step"
+    # incremental: grow each sequence token by token from scratch and compare bitwise
+    kl2 = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    kc2 = torch.zeros_like(kc)
+    grow = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    for L in range(1, max(lens) + 1, 7):
+        grow.copy_(torch.tensor([min(L, x) for x in lens], dtype=torch.int32))
+        S.seer_kcomp_update(dims, kd, wkd, grow, kl2, kc2, 1, 10000.0)
+    grow.copy_(seq)
+    for _ in range(3):
+        S.seer_kcomp_update(dims, kd, wkd, grow, kl2, kc2, 1, 10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(kl2, kl)
+    for b in range(B):
+        n = lens[b] // bs
+        assert torch.equal(kc2[b, :, :n], kc[b, :, :n])
+
+
+# --------------------------------------------------------------- the gate
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,dg,bs,lens", [
+    (1, 4, 1, 64, 64, 64, [1024]),
+    (3, 40, 8, 128, 128, 64, [4096, 1000, 64]),
+    (17, 32, 8, 128, 64, 128, [513 + 97 * i for i in range(17)]),
+])
+def test_gate_matches_oracle(S, B, Hq, Hkv, d, dg, bs, lens):
+    say(f"gate B={B} Hq={Hq} Hkv={Hkv} d={d} dg={dg} bs={bs}")
+    g = Hq // Hkv
+    lmax = max(lens) + 1
+    gen = torch.Generator().manual_seed(41 + B)
+    qn = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    k, _ = make_kv(B, Hkv, lmax, d, gen)
+    wq = (torch.randn((Hkv, dg, g * d), generator=gen) / math.sqrt(g * d)).to(torch.bfloat16)
+    wk = (torch.randn((Hkv, dg, 3 * d), generator=gen) / math.sqrt(3 * d)).to(torch.bfloat16)
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, lmax)
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=4, device=DEV)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    st.build_cache(k.to(DEV), wk.to(DEV), seq)
+    st.logits.fill_(float("nan"))
+    S.seer_gate_scores(dims, qn.to(DEV), wq.to(DEV), st.kcomp, st.kcomp_lens, seq, st.gate_ws,
+                       st.logits, 10000.0)
+    torch.cuda.synchronize()
+    qg = f64(st.q_gate)
+    lg = f64(st.logits)
+    kcg = f64(st.kcomp)
+    for b in range(B):
+        for h in range(Hkv):
+            ref_q = O.gate_query(f64(qn[b, h * g:(h + 1) * g]), f64(wq[h]), lens[b] - 1)
+            assert np.linalg.norm(qg[b, h] - ref_q) <= 1e-5 * np.linalg.norm(ref_q) + 1e-6
+            nc = lens[b] // bs
+            ref_z = O.gate_logits(ref_q, kcg[b, h, :nc])
+            assert np.max(np.abs(lg[b, h, :nc] - ref_z), initial=0.0) <= 1e-4
+            assert np.all(np.isneginf(lg[b, h, nc:]))
+
+
+# ------------------------------------------------------------ selection
+
+def _run_select(S, dims, z, kl, seq, mode, k, tau, max_sel):
+    B, Hkv = dims.batch, dims.num_kv_heads
+    zd = torch.from_numpy(z.astype(np.float32)).to(DEV)
+    idx = torch.full((B, Hkv, max_sel), 12345, dtype=torch.int32, device=DEV)
+    ns = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+    S.seer_select_blocks(dims, zd, torch.tensor(kl, dtype=torch.int32, device=DEV),
+                         torch.tensor(seq, dtype=torch.int32, device=DEV), mode, k, tau, max_sel,
+                         idx, ns)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), ns.cpu().numpy()
+
+
+@pytest.mark.parametrize("nbm,bs,k,quant", [(16, 64, 4, None), (512, 64, 64, None),
+                                            (512, 64, 52, 0.25), (2048, 64, 64, None),
+                                            (300, 128, 7, 1.0), (8192, 64, 100, None)])
+def test_select_topk_exact(S, nbm, bs, k, quant):
+    say(f"select topk nbm={nbm} k={k} quant={quant}")
+    B, Hkv = 5, 3
+    lmax = nbm * bs
+    rng = np.random.default_rng(nbm + k)
+    z = rng.normal(scale=2.0, size=(B, Hkv, nbm)).astype(np.float32)
+    if quant:  # many exact ties
+        z = (np.round(z / quant) * quant).astype(np.float32)
+    z[1, 0, 5] = -np.inf
+    z[1, 1, :] = 0.0
+    seq = [lmax, lmax - 5, 3 * bs + 1, bs - 1, 2 * bs]
+    kl = [lmax // bs, (lmax - 5) // bs, 1, 0, 2]  # sequence 2: cache lags by two blocks
+    max_sel = min(k + 3, nbm)
+    dims = S.make_dims(B, 8 * Hkv, Hkv, 128, 128, bs, lmax)
+    idx, ns = _run_select(S, dims, z, kl, seq, S.SELECT_TOPK, k, 0.0, max_sel)
+    for b in range(B):
+        nc = min(kl[b], seq[b] // bs)
+        for h in range(Hkv):
+            ref = O.select_topk(z[b, h, :nc].astype(np.float64), k, seq[b], bs, capacity=max_sel)
+            got = idx[b, h, :ns[b, h]]
+            assert got.tolist() == ref.tolist(), f"b={b} h={h}"
+            assert np.all(idx[b, h, ns[b, h]:] == -1)
+
+
+@pytest.mark.parametrize("nbm,bs,tau", [(512, 128, 0.01), (64, 64, 0.05), (2048, 64, 0.001),
+                                        (100, 128, 0.0), (100, 64, 1.0)])
+def test_select_threshold(S, nbm, bs, tau):
+    say(f"select threshold nbm={nbm} tau={tau}")
+    B, Hkv = 4, 3
+    lmax = nbm * bs
+    rng = np.random.default_rng(nbm)
+    z = rng.normal(scale=2.5, size=(B, Hkv, nbm)).astype(np.float32)
+    seq = [lmax - 1, lmax, 5 * bs + 3, bs // 2]
+    kl = [s // bs for s in seq]
+    dims = S.make_dims(B, 4 * Hkv, Hkv, 128, 128, bs, lmax)
+    idx, ns = _run_select(S, dims, z, kl, seq, S.SELECT_THRESHOLD, 0, tau, nbm)
+    for b in range(B):
+        nc = seq[b] // bs
+        for h in range(Hkv):
+            zz = z[b, h, :nc].astype(np.float64)
+            got = idx[b, h, :ns[b, h]].tolist()
+            ref = O.select_threshold(zz, tau, seq[b], bs).tolist()
+            if got != ref:
+                thr = threshold_value(zz, tau) if tau > 0 else -np.inf
+                diff = set(got) ^ set(ref)
+                assert all(abs(zz[j] - thr) <= 1e-3 for j in diff), f"b={b} h={h}"
+            assert np.all(idx[b, h, ns[b, h]:] == -1)
+
+
+# ----------------------------------------------------------- end to end
+
+def _run_workload_step(S, w, inp, num_split=0):
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, inp["k"].shape[2])
+    mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
+    st = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau,
+                      num_split=num_split, device=DEV)
+    seq = inp["seq_lens"]
+    # the cache already holds every complete block but the last, which this
+    # step's update appends (the step that completes a block)
+    st.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    out, lse = st.step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    torch.cuda.synchronize()
+    return st, out, lse
+
+
+def _check_pair(w, inp, st, b, h, what):
+    L = int(inp["seq_lens"][b])
+    g = w.group
+    ref = oracle_chain(inp, w, b, h, L, capacity=st.max_selected)
+    n = int(st.num_selected[b, h])
+    got = st.block_idx[b, h, :n].cpu().tolist()
+    nc = L // w.block_size
+    forced = list(range(nc, -(-L // w.block_size)))
+    if w.mode == "topk":
+        same = check_topk_set(got, ref["blocks"], ref["logits"], w.topk_blocks, nc, forced, what)
+    else:
+        same = got == ref["blocks"].tolist()
+        if not same:
+            thr = threshold_value(ref["logits"], w.tau)
+            diff = set(got) ^ set(ref["blocks"].tolist())
+            assert all(abs(ref["logits"][j] - thr) <= 1e-3 for j in diff), what
+    q, k, v, _, _ = host_inputs(inp, w, b, h, L)
+    o_ref, l_ref = (ref["o"], ref["lse"]) if same else O.sparse_decode_pair(
+        q, k, v, L, got, w.block_size, 1.0 / math.sqrt(w.head_dim))
+    assert_out_close(f64(st.out[b, h * g:(h + 1) * g]), o_ref, what)
+    assert_lse_close(f64(st.lse[b, h * g:(h + 1) * g]), l_ref, what)
+    return same
+
+
+def test_end_to_end_tiny(S):
+    w = WORKLOADS["tiny"]
+    for L in [1024, 1000, 63, 1, 64, 65]:
+        say(f"e2e tiny L={L}")
+        inp = {kk: (vv.to(DEV) if torch.is_tensor(vv) else vv)
+               for kk, vv in make_inputs(w.replace(seq_len=L)).items()}
+        st, out, lse = _run_workload_step(S, w, inp)
+        _check_pair(w, inp, st, 0, 0, f"tiny L={L}")
+
+
+@pytest.mark.parametrize("name,pairs", [("qwen3_8b_layer", None), ("qwen3_14b_b16", 10),
+                                        ("threshold_b128", 8)])
+def test_end_to_end_full_size_sampled(S, name, pairs):
+    w = WORKLOADS[name]
+    say(f"e2e full size {name}: generating inputs")
+    inp = make_inputs(w, device=DEV)
+    st, out, lse = _run_workload_step(S, w, inp)
+    say(f"e2e full size {name}: checking")
+    all_pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    rng = np.random.default_rng(0)
+    if pairs is not None:
+        all_pairs = [all_pairs[i] for i in rng.choice(len(all_pairs), size=pairs, replace=False)]
+    n_same = sum(_check_pair(w, inp, st, b, h, f"{name} b={b} h={h}") for b, h in all_pairs)
+    assert n_same >= len(all_pairs) // 2
+    # every output is finite and every lse finite
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_pipeline_steps_match_oracle(S):
+    """Several consecutive decode steps with appends, incremental cache updates."""
+    from workloads import append_token
+    w = WORKLOADS["pipeline_128k"].replace(batch=3, max_seq_len=4096, seq_len_range=(300, 700),
+                                           steps=70)
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    for step in range(w.steps):
+        append_token(inp, gen)
+        st.step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+                inp["seq_lens"])
+        if step % 23 == 0 or step == w.steps - 1:
+            torch.cuda.synchronize()
+            say(f"pipeline step {step}")
+            assert st.kcomp_lens.cpu().tolist() == [int(L) // 64 for L in inp["seq_lens"].cpu()]
+            for b in range(w.batch):
+                for h in (0, w.num_kv_heads - 1):
+                    _check_pair(w, inp, st, b, h, f"pipeline step={step} b={b} h={h}")
+
+
+# ----------------------------------------------------------- argument errors
+
+def test_binding_rejects_bad_shapes(S):
+    say("binding shape checks")
+    dims = S.make_dims(2, 8, 2, 128, 128, 64, 256)
+    q = torch.zeros((2, 8, 64), dtype=torch.bfloat16, device=DEV)  # wrong d
+    k = torch.zeros((2, 2, 256, 128), dtype=torch.bfloat16, device=DEV)
+    seq = torch.zeros((2,), dtype=torch.int32, device=DEV)
+    out = torch.zeros((2, 8, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        S.seer_dense_decode(dims, q, k, k, seq, 0.1, 1, None, out)
+    with pytest.raises(S.SeerError):
+        S.seer_decode_num_split(dims, 4, 500)
