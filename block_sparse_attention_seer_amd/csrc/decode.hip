@@ -10,8 +10,10 @@
 // Reasoning"): the same flash-decoding schedule along the GQA group.
 //
 // MI355X design (not the pages' H100 design):
-//   * one workgroup = 4 waves = one split of one (b, h); a wave walks every
-//     4th 64-token chunk of the split and keeps its own online softmax;
+//   * one workgroup = NW waves = one split of one (b, h).  The (b, h)'s
+//     active tokens form 16-token tiles; every wave of its S splits takes an
+//     even contiguous range of tiles (so the work is balanced to one tile)
+//     and walks it 64 tokens at a time with its own online softmax;
 //   * both contractions run on MFMA v_mfma_f32_16x16x32_bf16 with the g
 //     query heads of the group padded to 16:
 //       S^T[token][head] = K[token][:] . q[head][:]      (A = K rows straight
@@ -22,9 +24,12 @@
 //     never leaves registers.  V is loaded as 8-byte pieces (4 dims of one
 //     token) and the B operand (8 tokens of one dim) is assembled with
 //     byte permutes, so V never goes through LDS;
-//   * the 4 waves merge in LDS; the splits of a (b, h) merge in the same
-//     launch: the last workgroup to finish (device-scope counter) combines
-//     the per-split (lse, o) partials.
+//   * the waves of a split merge in LDS; with one split the workgroup writes
+//     the output directly, otherwise it writes an (lse, o) partial and a
+//     second small kernel merges the splits.  (Merging inside the launch
+//     would need device-scope release/acquire, which on gfx950 turns into
+//     L2 write-back / invalidate operations that serialise across
+//     workgroups -- measured far slower than a second launch.)
 #include "seer_device.hpp"
 #include "seer_internal.h"
 
@@ -39,9 +44,9 @@ struct DecodeParams {
   const int32_t* seq_lens;
   const int32_t* block_idx;
   const int32_t* num_selected;
-  int32_t* counters;
-  float* part_lse;
-  float* part_o;
+  int32_t* counters;  // [pairs] finished splits (merge in the decode launch), or null
+  float* part_lse;  // [pairs, S, G]   log2-domain lse of each split
+  float* part_o;    // [pairs, S, G, D] normalised split outputs
   uint16_t* out;
   float* lse;
   int64_t sb, sh;
@@ -50,27 +55,21 @@ struct DecodeParams {
   float scale_log2;  // softmax scale times log2(e): scores are kept in log2 units
 };
 
-constexpr int kWaves = 4;
-
-// Element j (0..3) of four packed bf16 values.
+// bf16 j (0..3) of a's four values in the low half, of b's in the high half.
 __device__ __forceinline__ uint32_t pick2(uint2 a, uint2 b, int j) {
-  // returns bf16 j of a in the low half and bf16 j of b in the high half
   const uint32_t x = (j < 2) ? a.x : a.y;
   const uint32_t y = (j < 2) ? b.x : b.y;
   return (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
 }
 
-template <int D, int BS, bool DENSE>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+template <int D, int BS, bool DENSE, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   constexpr int KS = D / 32;   // k-steps of the score contraction
   constexpr int VH = D / 64;   // 64-dim halves of the value contraction
-  constexpr int CPB = BS / 64; // 64-token chunks per block
 
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][16][D];
-  __shared__ float sm_lse[16];
-  __shared__ int sm_last;
+  extern __shared__ float sm_o[];  // [NW][G][D]
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
 
   const int S = p.num_split;
   const int pair = blockIdx.x / S;
@@ -94,10 +93,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     nslots = p.num_selected[pair];
     nslots = min(max(nslots, 0), p.max_sel);
   }
-  const int C = nslots * CPB;
-  const int per = (C + S - 1) / S;
-  const int c0 = split * per;
-  const int c1 = min(C, c0 + per);
+  // The pair's active tokens, block after block, form 16-token tiles
+  // (a block holds BS/16 of them); the S*NW waves of the pair each take an
+  // even, contiguous range of tiles and walk it four tiles at a time.
+  constexpr int TPB = BS / 16;
+  const int T = nslots * TPB;
+  const int GW = S * NW;
+  const int gw = split * NW + w;
+  const int ta = static_cast<int>(static_cast<int64_t>(T) * gw / GW);
+  const int tb = static_cast<int>(static_cast<int64_t>(T) * (gw + 1) / GW);
 
   const uint16_t* kb = p.k + b * p.sb + h * p.sh;
   const uint16_t* vb = p.v + b * p.sb + h * p.sh;
@@ -117,41 +121,65 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   f32x4_t oacc[VH * 4];
 #pragma unroll
   for (int t = 0; t < VH * 4; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int last = L - 1;
 
-  for (int c = c0 + w; c < c1; c += kWaves) {
-    const int slot = c / CPB;
-    const int sub = c - slot * CPB;
-    const int blk = DENSE ? slot : idx[slot];
-    if (blk < 0 || blk >= nblk) continue;  // invalid entry: skipped
-    const int t0 = blk * BS + sub * 64;
-    if (t0 >= L) continue;
-    const int last = L - 1;
+  for (int t = ta; t < tb; t += 4) {
+    // first token of each of the four tiles, or -1 (outside the range, an
+    // invalid index entry, or past the sequence)
+    int tok0[4];
+    bool any = false;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      int base = -1;
+      const int u = t + nt;
+      if (u < tb) {
+        const int slot = u / TPB;
+        const int blk = DENSE ? slot : idx[slot];
+        if (blk >= 0 && blk < nblk) {
+          const int t0 = blk * BS + (u - slot * TPB) * 16;
+          if (t0 < L) base = t0;
+        }
+      }
+      tok0[nt] = base;
+      any = any || base >= 0;
+    }
+    if (!any) continue;
 
-    // K rows 16*nt + ln, dims 32*s + 8*lq .. +7 (the A operand).
+    // K rows tok0 + ln, dims 32*s + 8*lq .. +7 (the A operand).
     uint4 kr[4][KS];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int row = min(t0 + 16 * nt + ln, last);
-      const uint16_t* kp = kb + row * p.st + 8 * lq;
+      if (tok0[nt] >= 0) {
+        const int row = min(tok0[nt] + ln, last);
+        const uint16_t* kp = kb + row * p.st + 8 * lq;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kr[nt][s] = ld16(kp + 32 * s);
+        for (int s = 0; s < KS; ++s) kr[nt][s] = ld16(kp + 32 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kr[nt][s] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    // V rows 16*nt + 4*lq + r, dims 64*hh + 4*ln .. +3.
+    // V rows tok0 + 4*lq + r, dims 64*hh + 4*ln .. +3.
     uint2 vr[4][4][VH];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = min(t0 + 16 * nt + 4 * lq + r, last);
-        const uint16_t* vp = vb + row * p.st + 4 * ln;
+        if (tok0[nt] >= 0) {
+          const int row = min(tok0[nt] + 4 * lq + r, last);
+          const uint16_t* vp = vb + row * p.st + 4 * ln;
 #pragma unroll
-        for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = ld8(vp + 64 * hh);
+          for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = ld8(vp + 64 * hh);
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = make_uint2(0u, 0u);
+        }
       }
     // Keep all K and V loads of the chunk in flight together: nothing below
     // may be scheduled above this point.
     __builtin_amdgcn_sched_barrier(0);
 
-    // Scores: sc[nt][r] = S[token t0 + 16 nt + 4 lq + r][head ln].
+    // Scores: sc[nt][r] = S[token tok0[nt] + 4 lq + r][head ln].
     f32x4_t sc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -165,15 +193,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tok = t0 + 16 * nt + 4 * lq + r;
+        const int tok = tok0[nt] + 4 * lq + r;
         float x = sc[nt][r] * p.scale_log2;
-        x = (tok <= last) ? x : -INFINITY;
+        x = (tok0[nt] >= 0 && tok <= last) ? x : -INFINITY;
         sc[nt][r] = x;
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: the chunk has a valid token
+    const float m_new = fmaxf(m_run, mx);  // finite: some tile holds a valid token
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
 
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     }
 
     // O[head][64 hh + 4 ln + j] += P[head][tokens] . V[tokens][..]; the 8
-    // tokens of k-group lq in step s2 are 16*(2 s2 + kk/4) + 4 lq + kk%4.
+    // tokens of k-group lq in step s2 are tok0[2 s2 + kk/4] + 4 lq + kk%4.
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const uint4 pa = make_uint4(pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]);
@@ -221,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // ---- merge the 4 waves of this split
+  // ---- merge the waves of this split
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (lq == 0) {
@@ -235,108 +263,187 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int r2 = 0; r2 < 4; ++r2) {
         const int head = 4 * lq + r2;
-        if (head < G) sm_o[w][head][64 * hh + 4 * ln + j] = oacc[hh * 4 + j][r2];
+        if (head < G) sm_o[(w * G + head) * D + 64 * hh + 4 * ln + j] = oacc[hh * 4 + j][r2];
       }
   __syncthreads();
 
   const int nel = G * D;
-  const int64_t out_base = (static_cast<int64_t>(b) * p.Hq + h * G);
-  if (S == 1) {
-    for (int e = tid; e < nel; e += 256) {
-      const int head = e / D;
-      const int dim = e - head * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][head]);
-      float osum = 0.f, lsum = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          const float mw = sm_m[ww][head];
-          const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-          osum += f * sm_o[ww][head][dim];
-          lsum += f * sm_l[ww][head];
-        }
-      }
-      const bool any = lsum > 0.f;
-      p.out[(out_base + head) * D + dim] = f2bf(any ? osum / lsum : 0.f);
-      if (dim == 0 && p.lse != nullptr)
-        p.lse[out_base + head] = any ? (M + fast_log2(lsum)) * kLn2 : -INFINITY;
-    }
-    return;
-  }
-
+  const int64_t out_base = static_cast<int64_t>(b) * p.Hq + h * G;
   const int64_t part = static_cast<int64_t>(pair) * S + split;
-  for (int e = tid; e < nel; e += 256) {
+  for (int e = tid; e < nel; e += NW * 64) {
     const int head = e / D;
     const int dim = e - head * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][head]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][head]);
     float osum = 0.f, lsum = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const float mw = sm_m[ww][head];
         const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        osum += f * sm_o[ww][head][dim];
+        osum += f * sm_o[(ww * G + head) * D + dim];
         lsum += f * sm_l[ww][head];
       }
     }
     const bool any = lsum > 0.f;
-    p.part_o[(part * G + head) * D + dim] = any ? osum / lsum : 0.f;
-    if (dim == 0) p.part_lse[part * G + head] = any ? M + fast_log2(lsum) : -INFINITY;
+    const float o = any ? osum / lsum : 0.f;
+    if (S == 1) {
+      p.out[(out_base + head) * D + dim] = f2bf(o);
+      if (dim == 0 && p.lse != nullptr)
+        p.lse[out_base + head] = any ? (M + fast_log2(lsum)) * kLn2 : -INFINITY;
+    } else if (p.counters == nullptr) {
+      p.part_o[(part * G + head) * D + dim] = o;
+      if (dim == 0) p.part_lse[part * G + head] = any ? M + fast_log2(lsum) : -INFINITY;
+    } else {
+      // device-coherent stores (they write through the per-XCD L2)
+      __hip_atomic_store(&p.part_o[(part * G + head) * D + dim], o, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (dim == 0)
+        __hip_atomic_store(&p.part_lse[part * G + head], any ? M + fast_log2(lsum) : -INFINITY,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+  if (S == 1 || p.counters == nullptr) return;
 
-  // ---- the last split of this (b, h) to finish combines all splits
+  // ---- the last split of this (b, h) to finish merges all splits.
+  // Partials travel only through device-coherent stores and loads, so the
+  // hand-off needs no cache write-back or invalidation: each thread waits
+  // until its stores are performed, the workgroup then counts itself on a
+  // device-scope counter, and the workgroup that completes the count reads
+  // the partials back coherently.
+  __shared__ int sm_last;
+  __shared__ float sm_w[kMaxSplit * 16];
+  __shared__ float sm_lse[16];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const int prev = __hip_atomic_fetch_add(p.counters + pair, 1, __ATOMIC_ACQ_REL,
+    const int prev = __hip_atomic_fetch_add(p.counters + pair, 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     sm_last = (prev == S - 1);
   }
   __syncthreads();
   if (!sm_last) return;
-  __threadfence();
-
-  float* wts = &sm_o[0][0][0];  // S * G <= 128 * 16 floats fit in sm_o
   const float* plse = p.part_lse + static_cast<int64_t>(pair) * S * G;
+  const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
+  for (int i = tid; i < S * G; i += NW * 64)
+    sm_w[i] = __hip_atomic_load(plse + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
   if (tid < G) {
     const int head = tid;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, plse[s * G + head]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, sm_w[s * G + head]);
     float tot = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const float ls = plse[s * G + head];
-        const float f = (ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
-        wts[s * G + head] = f;
-        tot += f;
-      }
-    } else {
-      for (int s = 0; s < S; ++s) wts[s * G + head] = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ls = sm_w[s * G + head];
+      const float f = (M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
+      sm_w[s * G + head] = f;
+      tot += f;
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    for (int s = 0; s < S; ++s) wts[s * G + head] *= inv;
+    for (int s = 0; s < S; ++s) sm_w[s * G + head] *= inv;
     sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
-  for (int e = tid; e < nel; e += 256) {
+  for (int e = tid; e < nel; e += NW * 64) {
     const int head = e / D;
     const int dim = e - head * D;
     float o = 0.f;
-    for (int s = 0; s < S; ++s) o += wts[s * G + head] * po[(s * G + head) * D + dim];
+    for (int s = 0; s < S; ++s)
+      o += sm_w[s * G + head] *
+           __hip_atomic_load(po + (s * G + head) * D + dim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     p.out[(out_base + head) * D + dim] = f2bf(o);
     if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
   }
   if (tid == 0) __hip_atomic_store(p.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int BS, bool DENSE>
+// Merge of the splits of one (b, h): o = sum_s w_s o_s with
+// w_s = exp2(lse_s - M) / sum_s' exp2(lse_s' - M).  Each thread first issues
+// the loads of all its split outputs (independent of the weights), then the
+// lse values are reduced while those loads are in flight.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineMaxS = 8;  // split outputs held in registers per pass
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p) {
+  __shared__ float sm_w[kMaxSplit * 16];
+  __shared__ float sm_lse[16];
+  const int pair = blockIdx.x;
+  const int S = p.num_split;
+  const int G = p.G;
+  const int b = pair / p.Hkv;
+  const int h = pair - b * p.Hkv;
+  const int tid = threadIdx.x;
+  const float* plse = p.part_lse + static_cast<int64_t>(pair) * S * G;
+  const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
+  const int64_t out_base = static_cast<int64_t>(b) * p.Hq + h * G;
+  const int nel = G * D;
+
+  // element e = tid + 256 i (i < 4 covers G*D <= 16*64; D=128 needs i < 8)
+  constexpr int EPT = 16 * D / kCombineThreads;
+  float pre[EPT][kCombineMaxS];
+  const int s_pre = min(S, kCombineMaxS);
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + kCombineThreads * i;
+    const int head = e / D;
+#pragma unroll
+    for (int s = 0; s < kCombineMaxS; ++s)
+      pre[i][s] = (e < nel && s < s_pre) ? po[(s * G + head) * D + (e - head * D)] : 0.f;
+  }
+  for (int i = tid; i < S * G; i += kCombineThreads) sm_w[i] = plse[i];
+  __syncthreads();
+  if (tid < G) {
+    const int head = tid;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, sm_w[s * G + head]);
+    float tot = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ls = sm_w[s * G + head];
+      const float f = (M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
+      sm_w[s * G + head] = f;
+      tot += f;
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    for (int s = 0; s < S; ++s) sm_w[s * G + head] *= inv;
+    sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + kCombineThreads * i;
+    if (e >= nel) break;
+    const int head = e / D;
+    const int dim = e - head * D;
+    float o = 0.f;
+#pragma unroll
+    for (int s = 0; s < kCombineMaxS; ++s)
+      if (s < s_pre) o += sm_w[s * G + head] * pre[i][s];
+    for (int s = kCombineMaxS; s < S; ++s) o += sm_w[s * G + head] * po[(s * G + head) * D + dim];
+    p.out[(out_base + head) * D + dim] = f2bf(o);
+    if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
+  }
+}
+
+template <int D, int BS, bool DENSE, int NW>
 void launch_one(const DecodeParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE>), dim3(grid), dim3(256), 0, stream, p);
+  const size_t lds = static_cast<size_t>(NW) * p.G * D * sizeof(float);
+  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW>), dim3(grid), dim3(NW * 64), lds, stream, p);
+}
+
+template <int NW>
+void launch_variant(int key, const DecodeParams& p, int grid, hipStream_t s) {
+  switch (key) {
+    case 0: launch_one<64, 64, false, NW>(p, grid, s); break;
+    case 1: launch_one<64, 64, true, NW>(p, grid, s); break;
+    case 2: launch_one<64, 128, false, NW>(p, grid, s); break;
+    case 3: launch_one<64, 128, true, NW>(p, grid, s); break;
+    case 4: launch_one<128, 64, false, NW>(p, grid, s); break;
+    case 5: launch_one<128, 64, true, NW>(p, grid, s); break;
+    case 6: launch_one<128, 128, false, NW>(p, grid, s); break;
+    default: launch_one<128, 128, true, NW>(p, grid, s); break;
+  }
 }
 
 }  // namespace
@@ -364,13 +471,14 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   p.max_sel = a.max_selected;
   p.num_split = S;
   p.scale_log2 = a.scale * kLog2e;
+  const bool inline_merge = a.merge_inline;
   if (S > 1) {
     char* ws = static_cast<char*>(a.workspace);
     size_t cbytes = static_cast<size_t>(pairs) * sizeof(int32_t);
     cbytes = (cbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
     size_t lbytes = static_cast<size_t>(pairs) * S * G * sizeof(float);
     lbytes = (lbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
-    p.counters = reinterpret_cast<int32_t*>(ws);
+    p.counters = inline_merge ? reinterpret_cast<int32_t*>(ws) : nullptr;
     p.part_lse = reinterpret_cast<float*>(ws + cbytes);
     p.part_o = reinterpret_cast<float*>(ws + cbytes + lbytes);
   }
@@ -383,20 +491,28 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dense = (a.block_idx == nullptr);
   const int key = (d.head_dim == 128 ? 4 : 0) | (d.block_size == 128 ? 2 : 0) | (dense ? 1 : 0);
-  switch (key) {
-    case 0: launch_one<64, 64, false>(p, grid, s); break;
-    case 1: launch_one<64, 64, true>(p, grid, s); break;
-    case 2: launch_one<64, 128, false>(p, grid, s); break;
-    case 3: launch_one<64, 128, true>(p, grid, s); break;
-    case 4: launch_one<128, 64, false>(p, grid, s); break;
-    case 5: launch_one<128, 64, true>(p, grid, s); break;
-    case 6: launch_one<128, 128, false>(p, grid, s); break;
-    default: launch_one<128, 128, true>(p, grid, s); break;
-  }
-  const hipError_t e = hipGetLastError();
+  const int nw = (a.waves_per_group == 4 || (a.waves_per_group == 8 && G <= 8))
+                     ? a.waves_per_group
+                     : decode_waves_per_group(pairs, S, G);
+  if (nw == 8)
+    launch_variant<8>(key, p, grid, s);
+  else
+    launch_variant<4>(key, p, grid, s);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error(std::string("decode launch: ") + hipGetErrorString(e));
     return SEER_ERR_HIP;
+  }
+  if (S > 1 && !inline_merge) {
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL(combine_kernel<128>, dim3(grid64 / S), dim3(kCombineThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(combine_kernel<64>, dim3(grid64 / S), dim3(kCombineThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      set_error(std::string("combine launch: ") + hipGetErrorString(e));
+      return SEER_ERR_HIP;
+    }
   }
   return SEER_OK;
 }

@@ -105,20 +105,30 @@ size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim)
 }
 
 int auto_num_split(const seer_dims* d, int max_blocks, int num_cus) {
-  // 64-token chunks each (b, h) may have to visit.
-  const int64_t chunks = static_cast<int64_t>(max_blocks) * (d->block_size / 64);
+  // Measured on MI355X: the decode kernel saturates HBM with about eight
+  // waves per compute unit, and one compute unit alone sustains only about
+  // 28 GB/s, so every CU needs work.  Aim at 8 waves per CU in total, using
+  // the workgroup size the launcher picks, but give each workgroup at least
+  // one 64-token chunk.
+  const int g = d->num_q_heads / d->num_kv_heads;
   const int64_t pairs = static_cast<int64_t>(d->batch) * d->num_kv_heads;
-  // Aim at about four workgroups (of four waves) per compute unit so the
-  // scheduler can balance uneven splits, but keep at least eight chunks
-  // (two per wave) in a split so that the partials stay a small fraction
-  // of the traffic.
-  const int64_t target_wgs = 4LL * (num_cus > 0 ? num_cus : 256);
+  const int64_t chunks = static_cast<int64_t>(max_blocks) * (d->block_size / 64);
+  const int cus = num_cus > 0 ? num_cus : 256;
+  const int nw = decode_waves_per_group(pairs, 1, g);
+  const int64_t target_wgs = static_cast<int64_t>(cus) * 8 / nw;
   int64_t s = (target_wgs + pairs - 1) / pairs;
-  const int64_t cap = (chunks + 7) / 8;
-  if (s > cap) s = cap;
+  if (s > chunks) s = chunks;
   if (s < 1) s = 1;
   if (s > kMaxSplit) s = kMaxSplit;
   return static_cast<int>(s);
+}
+
+int decode_waves_per_group(int64_t pairs, int num_split, int g) {
+  // Eight waves per workgroup whenever the wave merge fits 32 KiB of LDS
+  // (g <= 8), four otherwise.
+  (void)pairs;
+  (void)num_split;
+  return g <= 8 ? 8 : 4;
 }
 
 }  // namespace seer

@@ -14,7 +14,7 @@ namespace seer {
 constexpr int kMaxGroup = 16;          // query heads per KV head (MFMA N = 16)
 constexpr int kMaxNBSelect = 8192;     // blocks per sequence the select kernel holds in LDS
 constexpr int kMaxSplit = 128;         // splits per (b, h) in the decode kernel
-constexpr int kCounterBytes = 256;     // alignment of the partials after the counters
+constexpr int kCounterBytes = 256;     // alignment of the partial outputs after the partial lse
 
 // ------------------------------------------------------- argument checks
 // These live in a HIP-free translation unit so that a CPU-only test can
@@ -27,7 +27,7 @@ int check_ptr(const void* p, size_t align, const char* name, std::string* why);
 int64_t nb_max(const seer_dims* d);  // ceil(Lmax / b)
 size_t gate_workspace_bytes(const seer_dims* d);
 // Workspace of the decode kernel for `pairs` (b, h) pairs, `num_split`
-// splits and group size g.
+// splits and group size g: the per-split lse and outputs.
 size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim);
 // Automatic split count given the device's compute-unit count.
 int auto_num_split(const seer_dims* d, int max_blocks, int num_cus);
@@ -83,11 +83,16 @@ struct DecodeArgs {
   int max_selected;             // index row length (sparse)
   float scale;
   int num_split;
+  int waves_per_group;          // 0 = automatic (4 or 8)
+  bool merge_inline;            // merge splits in the decode launch (counters in the workspace)
   void* workspace;
   uint16_t* out;
   float* lse;
 };
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
+
+// Waves per decode workgroup chosen automatically.
+int decode_waves_per_group(int64_t pairs, int num_split, int g);
 
 // Device query (HIP): compute units of the current device, cached.
 int device_cu_count(int* out);

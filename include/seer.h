@@ -177,9 +177,11 @@ int seer_select_blocks(const seer_dims* dims, const float* logits,
                        int32_t* num_selected, void* stream);
 
 /*
- * Decode workspace: split partials plus one completion counter per
- * (b, h).  `max_blocks` is max_selected (sparse) or NBmax (dense);
- * `num_split` 0 means "choose automatically" (queries the current device).
+ * Decode workspace: one completion counter per (b, h) followed by the
+ * per-split partial results (lse and output of each split of each (b, h));
+ * 0 bytes when the call uses one split.  `max_blocks` is max_selected
+ * (sparse) or NBmax (dense); `num_split` 0 means "choose automatically"
+ * (queries the current device).
  * The counters must be ZERO before the first call that uses a workspace;
  * every call leaves them zero again, so one zero-fill at allocation is
  * enough.  One workspace must not be used by two calls that can run at the
@@ -198,7 +200,8 @@ int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks,
  * [CP Knowl 6]: grid (batch, heads_kv, num_split); the work of each
  * (b, h) is split along num_split from its list of active blocks, the kernel
  * loops only over active indices and skips invalid entries; [PN key design
- * 4] same.  Split results are merged by log-sum-exp in the same launch.
+ * 4] same.  With more than one split, the last split of each (b, h) to
+ * finish merges the splits by log-sum-exp in the same launch.
  *
  * For each query head hq = h*g + i of sequence b: over the tokens
  * T = union over the first num_selected[b,h] entries j of block_idx[b,h] with
@@ -212,7 +215,8 @@ int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks,
  *              by seer_select_blocks; indices must not repeat).
  *   scale      usually 1/sqrt(d).   num_split 0 = automatic.
  *   workspace  >= seer_decode_workspace_bytes(dims, max_selected, num_split)
- *              bytes, 256-byte aligned, counters zero (see above).
+ *              bytes, 256-byte aligned, counters zero (see above); may be
+ *              NULL when that size is 0.
  */
 int seer_sparse_decode(const seer_dims* dims, const uint16_t* q,
                        const uint16_t* k_cache, const uint16_t* v_cache,

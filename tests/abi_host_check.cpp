@@ -71,18 +71,23 @@ int main() {
   EXPECT(seer::nb_max(&d) == 513);
   d = good();
   EXPECT(seer::gate_workspace_bytes(&d) == 16u * 8 * 128 * 4);
-  // one split needs no workspace; otherwise counters + lse + o, 256-aligned
+  // one split needs no workspace; otherwise counters + lse (each 256-aligned) + o
   EXPECT(seer::decode_workspace_bytes(128, 1, 5, 128) == 0);
   const size_t ws = seer::decode_workspace_bytes(128, 4, 5, 128);
   EXPECT(ws == 512 + 10240 + 128u * 4 * 5 * 128 * 4);
-  // automatic split: at least 1, at most 128, and it fills 256 compute units
-  const int s3 = seer::auto_num_split(&d, 53, 256);
-  EXPECT(s3 >= 1 && s3 <= 128);
-  EXPECT(128 * s3 >= 256);
+  EXPECT(seer::decode_workspace_bytes(3, 2, 1, 64) == 256 + 256 + 3u * 2 * 64 * 4);
+  // automatic split: about 8 waves per compute unit in total (8-wave
+  // workgroups for g <= 8), at most one split per 64-token chunk
+  EXPECT(seer::decode_waves_per_group(128, 2, 5) == 8);
+  EXPECT(seer::decode_waves_per_group(128, 2, 16) == 4);
+  EXPECT(seer::auto_num_split(&d, 53, 256) == 2);     // 128 pairs x 2 x 8 waves
   seer_dims one = good();
   one.batch = 1;
-  const int s2 = seer::auto_num_split(&one, 65, 256);
-  EXPECT(s2 >= 1 && s2 <= (65 + 7) / 8);
+  EXPECT(seer::auto_num_split(&one, 65, 256) == 32);  // 8 pairs fill 256 CUs
+  EXPECT(seer::auto_num_split(&one, 3, 256) == 3);    // never more splits than chunks
+  seer_dims wide = good();
+  wide.num_q_heads = 128;                             // g = 16: 4-wave groups
+  EXPECT(seer::auto_num_split(&wide, 53, 256) == 4);
 
   if (failures == 0) std::printf("abi host checks: all passed\n");
   return failures == 0 ? 0 : 1;

@@ -109,7 +109,7 @@ def test_sparse_decode_matches_oracle(S, d, bs, Hq, Hkv, lens, num_split):
             o_ref, l_ref = O.sparse_decode_pair(qq, kk, vv, lens[b], blocks, bs, scale)
             assert_out_close(og[b, h * g:(h + 1) * g], o_ref, f"b={b} h={h}")
             assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, f"b={b} h={h}")
-    # the counters in the workspace are left at zero
+    # the completion counters in the workspace are left at zero
     if ns > 1:
         assert int(ws[: B * Hkv].view(torch.int32).abs().sum()) == 0
 
