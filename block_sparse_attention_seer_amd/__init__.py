@@ -32,8 +32,9 @@ __all__ = [
     "SELECT_TOPK", "SELECT_THRESHOLD", "make_dims",
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
-    "seer_sparse_decode", "seer_dense_decode", "seer_status_string",
-    "seer_last_error_message", "seer_version", "DecodeStep",
+    "seer_sparse_decode", "seer_dense_decode", "seer_decode_step_workspace_bytes",
+    "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
+    "DecodeStep",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,8 +47,8 @@ SELECT_THRESHOLD = 2
 EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
-    "seer_sparse_decode", "seer_dense_decode", "seer_status_string",
-    "seer_last_error_message", "seer_version",
+    "seer_sparse_decode", "seer_dense_decode", "seer_decode_step_workspace_bytes",
+    "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
 )
 
 
@@ -96,6 +97,10 @@ _SIGS = {
                                   ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
     "seer_dense_decode": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, ctypes.c_float, _I32,
                                  _P, ctypes.c_size_t, _P, _P, _P]),
+    "seer_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SeerDims), _I32, _I32]),
+    "seer_decode_step": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _I32, ctypes.c_double, _I32, _I32, ctypes.c_float, _I32, _P, _P,
+                                _P, ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
     "seer_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "seer_last_error_message": (ctypes.c_char_p, []),
     "seer_version": (ctypes.c_char_p, []),
@@ -283,6 +288,37 @@ def seer_dense_decode(dims: SeerDims, q, k_cache, v_cache, seq_lens, scale: floa
                                    _ptr(lse), _stream(q)), "seer_dense_decode")
 
 
+def seer_decode_step_workspace_bytes(dims: SeerDims, max_selected: int, num_split: int = 0) -> int:
+    return int(lib().seer_decode_step_workspace_bytes(ctypes.byref(dims), int(max_selected),
+                                                      int(num_split)))
+
+
+def seer_decode_step(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                     kcomp_lens, kcomp, max_new_blocks: int, rope_theta: float, mode: int,
+                     topk_blocks: int, threshold: float, max_selected: int, block_idx,
+                     num_selected, logits, scale: float, num_split: int, workspace, out,
+                     lse=None) -> None:
+    B, Hq, Hkv, d, dg = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim, dims.d_gate
+    dev = q.device
+    _check_decode_io(dims, q, k_cache, v_cache, seq_lens, out, lse)
+    _need(q_nope, "q_nope", torch.bfloat16, (B, Hq, d), dev)
+    _check_kv(dims, k_nope, "k_nope")
+    _need(w_q, "w_q", torch.bfloat16, (Hkv, dg, dims.group * d), dev)
+    _need(w_k, "w_k", torch.bfloat16, (Hkv, dg, 3 * d), dev)
+    _need(kcomp_lens, "kcomp_lens", torch.int32, (B,), dev)
+    _need(kcomp, "kcomp", torch.bfloat16, (B, Hkv, dims.nb_max, dg), dev)
+    _need(block_idx, "block_idx", torch.int32, (B, Hkv, max_selected), dev)
+    _need(num_selected, "num_selected", torch.int32, (B, Hkv), dev)
+    _need(logits, "logits", torch.float32, (B, Hkv, dims.nb_max), dev)
+    wp, wn = _ws(workspace, dev)
+    _check(lib().seer_decode_step(
+        ctypes.byref(dims), _ptr(q_nope), _ptr(q), _ptr(k_nope), _ptr(k_cache), _ptr(v_cache),
+        _ptr(w_q), _ptr(w_k), _ptr(seq_lens), _ptr(kcomp_lens), _ptr(kcomp), int(max_new_blocks),
+        float(rope_theta), int(mode), int(topk_blocks), float(threshold), int(max_selected),
+        _ptr(block_idx), _ptr(num_selected), _ptr(logits), float(scale), int(num_split), wp, wn,
+        _ptr(out), _ptr(lse), _stream(q)), "seer_decode_step")
+
+
 class DecodeStep:
     """Buffers and calls of one layer's decode step (allocation via torch).
 
@@ -319,6 +355,8 @@ class DecodeStep:
         self.decode_ws = torch.zeros((max(dws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, Hq, dims.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        sws = seer_decode_step_workspace_bytes(dims, self.max_selected, self.num_split)
+        self.step_ws = torch.zeros((max(sws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
 
     @property
     def q_gate(self) -> torch.Tensor:
@@ -346,4 +384,17 @@ class DecodeStep:
         seer_sparse_decode(d, q, k_cache, v_cache, seq_lens, self.block_idx, self.num_selected,
                            self.max_selected, scale, self.num_split, self.decode_ws, self.out,
                            self.lse)
+        return self.out, self.lse
+
+    def fused_step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                   scale: Optional[float] = None, max_new_blocks: int = 1):
+        """The same step through seer_decode_step (fewer launches)."""
+        d = self.dims
+        if scale is None:
+            scale = 1.0 / math.sqrt(d.head_dim)
+        seer_decode_step(d, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                         self.kcomp_lens, self.kcomp, max_new_blocks, self.rope_theta, self.mode,
+                         self.topk_blocks, self.threshold, self.max_selected, self.block_idx,
+                         self.num_selected, self.logits, scale, self.num_split, self.step_ws,
+                         self.out, self.lse)
         return self.out, self.lse

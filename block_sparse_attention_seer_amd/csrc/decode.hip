@@ -53,6 +53,9 @@ struct DecodeParams {
   int st;
   int Hq, Hkv, G, Lmax, max_sel, num_split;
   float scale_log2;  // softmax scale times log2(e): scores are kept in log2 units
+  // fused step: workgroup 0 raises the cache counters of every sequence
+  int32_t* commit_lens;
+  int commit_max_new, B, BS, NBmax;
 };
 
 // bf16 j (0..3) of a's four values in the low half, of b's in the high half.
@@ -82,6 +85,14 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   const int ln = lane & 15;
   const int lq = lane >> 4;
   const int G = p.G;
+
+  // Fused step: the cache entries appended by this step's gate launch are
+  // counted now, after every reader of the old count has finished.
+  if (p.commit_lens != nullptr && blockIdx.x == 0) {
+    for (int bb = tid; bb < p.B; bb += NW * 64)
+      p.commit_lens[bb] = committed_count(p.seq_lens[bb], p.commit_lens[bb], p.BS, p.Lmax, p.NBmax,
+                                          p.commit_max_new);
+  }
 
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.Lmax);
@@ -471,6 +482,11 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   p.max_sel = a.max_selected;
   p.num_split = S;
   p.scale_log2 = a.scale * kLog2e;
+  p.commit_lens = a.commit_lens;
+  p.commit_max_new = a.commit_max_new;
+  p.B = d.batch;
+  p.BS = d.block_size;
+  p.NBmax = static_cast<int>(nb_max(&d));
   const bool inline_merge = a.merge_inline;
   if (S > 1) {
     char* ws = static_cast<char*>(a.workspace);

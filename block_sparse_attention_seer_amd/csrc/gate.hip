@@ -1,108 +1,209 @@
-// AttnGate block scoring for one decode step, for gfx950 (MI355X).
+// AttnGate kernels of the decode step, for gfx950 (MI355X).
 //
 // [CP Knowl 1, Knowl 2] (chapterpal page "SeerAttention-R: Sparse Attention
-// Adaptation for Long Reasoning"): the query branch maps the g query heads
-// of each GQA group, concatenated to g*d values, through one linear layer
-// W_q (d_gate x g*d) to one gate query, re-applies RoPE, and scores it
-// against the compressed keys as Q_gate K_gate^T / sqrt(d_gate).
-// [PN key design 1] (papernotes page "Sparse Attention Adaptation for Long
-// Reasoning"): one W_q per KV head.
+// Adaptation for Long Reasoning"): gate query Q_gate = RoPE(W_q reshape(Q_nope,
+// [.., g*d])), compressed keys K_gate = RoPE(W_k [P_max, P_min, P_avg](K_nope)),
+// block scores Q_gate K_gate^T / sqrt(d_gate).  [PN key design 1] (papernotes
+// page "Sparse Attention Adaptation for Long Reasoning"): one W_q per KV head.
+// [CP Knowl 5]: the K Compression Cache gets one entry per newly completed
+// block, once every b tokens; top-k or threshold then picks the blocks.
 //
-// Two kernels:
-//   qgate_kernel   Q_gate[b, h] = RoPE(W_q[h] . concat(q_nope group), L_b - 1)
-//                  as one small GEMM per KV head on MFMA (rows of W_q x batch),
-//                  reading W_q once per step; RoPE angles in float64.
-//   logits_kernel  z[b, h, j] = Q_gate . kcomp[b, h, j] / sqrt(d_gate), float32
-//                  VALU dot products, 16-byte coalesced rows of the cache.
+// Kernels:
+//   prep_kernel    one launch for two kinds of independent tasks:
+//                  * gate-query tiles: 16 gate rows x 16 sequences of one KV
+//                    head as an MFMA GEMM (W_q read once per step, not once
+//                    per sequence), the g*d contraction split over 4 waves
+//                    with every load issued up front, then RoPE in float64;
+//                  * cache-entry tasks: one newly completed block of one
+//                    (sequence, KV head) each (pool, W_k GEMV, RoPE, bf16).
+//   gate_kernel    one 512-thread workgroup per (sequence, KV head): all its
+//                  cache rows requested at once, block logits in float32,
+//                  and -- in the fused step -- the selection, from LDS.
+//   commit_kernel  raises kcomp_lens once every new entry is written.
 #include <cmath>
 
-#include "seer_device.hpp"
+#include "gate_dev.hpp"
+#include "select_dev.hpp"
 #include "seer_internal.h"
 
 namespace seer {
 
 namespace {
 
-struct QgateParams {
+RopeFreqs make_freqs(int dg, double theta) {
+  RopeFreqs f{};
+  for (int i = 0; i < dg / 2; ++i) f.w[i] = std::pow(theta, -2.0 * i / dg);
+  return f;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return SEER_ERR_HIP;
+  }
+  return SEER_OK;
+}
+
+// ------------------------------------------------ gate query + cache entries
+
+struct PrepParams {
+  // gate-query tiles (n_query_wgs of them, first in the grid)
   const uint16_t* q_nope;
   const uint16_t* w_q;
-  const int32_t* seq_lens;
   float* q_gate;
-  int B, Hq, Hkv, G, D, DG, Lmax;
-  double theta;
+  int n_query_wgs;
+  // cache-entry tasks (the rest of the grid): entry kcomp_lens[b] + z
+  const uint16_t* k_nope;
+  const uint16_t* w_k;
+  const int32_t* kcomp_lens;
+  uint16_t* kcomp;
+  int max_new;
+  const int32_t* seq_lens;
+  int64_t sb, sh, st;
+  int B, Hq, Hkv, G, BS, Lmax, NBmax;
+  RopeFreqs freqs;
 };
 
-// grid (H_kv, d_gate/16, ceil(B/16)), one wave.  The 16 rows of the MFMA
-// M-tile are gate rows i0..i0+7 and their RoPE partners i0+DG/2..i0+DG/2+7,
-// so each rotation pairs lane l with lane l^32.
-__global__ __launch_bounds__(64) void qgate_kernel(QgateParams p) {
-  const int h = blockIdx.x;
-  const int i0 = blockIdx.y * 8;
-  const int bt = blockIdx.z * 16;
-  const int lane = threadIdx.x;
+constexpr int kQueryStepsPerWave = 16;  // k-steps of 32 per wave: g*d <= 2048
+
+// Gate-query tile t: 16 gate rows (rows i0..i0+7 and their RoPE partners
+// i0+DG/2..) x 16 sequences of one KV head as MFMA D = W_q . X.  The 4 waves
+// split the g*d contraction; each issues all of its loads before its first
+// MFMA; the partial tiles are summed in a fixed order.
+template <int D, int DG>
+__device__ void query_tile(const PrepParams& p, int t, float (*red)[64][4]) {
+  const int RT = DG / 16;
+  const int BT = (p.B + 15) / 16;
+  const int h = t / (RT * BT);
+  const int rt = (t / BT) % RT;
+  const int b0 = (t % BT) * 16;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
   const int ln = lane & 15;
   const int lq = lane >> 4;
-  const int half = p.DG >> 1;
-  const int K = p.G * p.D;  // multiple of 64
+  const int half = DG / 2;
+  const int i0 = rt * 8;
+  const int K = p.G * D;
+  const int KST = K / 32;
+
+  const int bq = b0 + ln;
+  const bool bvalid = bq < p.B;
+  int L = bvalid ? p.seq_lens[bq] : 1;  // issued early; used by the rotation
 
   const int arow = (ln < 8) ? (i0 + ln) : (half + i0 + ln - 8);
-  const uint16_t* wrow = p.w_q + (static_cast<int64_t>(h) * p.DG + arow) * K + 8 * lq;
-  const int bq = bt + ln;
-  const bool bvalid = bq < p.B;
-  const uint16_t* xrow =
-      p.q_nope + (static_cast<int64_t>(bvalid ? bq : 0) * p.Hq + h * p.G) * p.D + 8 * lq;
-
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const uint4 a = ld16(wrow + k0);
-    const uint4 x = bvalid ? ld16(xrow + k0) : make_uint4(0u, 0u, 0u, 0u);
-    acc = mfma16x16x32(a, x, acc);
+  const uint16_t* wrow = p.w_q + (static_cast<int64_t>(h) * DG + arow) * K + 8 * lq;
+  const uint16_t* xrow = p.q_nope + (static_cast<int64_t>(bvalid ? bq : 0) * p.Hq + h * p.G) * D + 8 * lq;
+  const int s0 = w * KST / 4;
+  const int s1 = (w + 1) * KST / 4;
+  uint4 a[kQueryStepsPerWave], x[kQueryStepsPerWave];
+#pragma unroll
+  for (int i = 0; i < kQueryStepsPerWave; ++i) {
+    const int s = s0 + i;
+    a[i] = (s < s1) ? ld16(wrow + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
+    x[i] = (s < s1 && bvalid) ? ld16(xrow + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
   }
-  // acc[r] = Y[tile row 4*lq + r][batch bt + ln]
-  int L = bvalid ? p.seq_lens[bq] : 1;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kQueryStepsPerWave; ++i)
+    if (s0 + i < s1) acc = mfma16x16x32(a[i], x[i], acc);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[w][lane][r] = acc[r];
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    acc[r] = ((red[0][lane][r] + red[1][lane][r]) + red[2][lane][r]) + red[3][lane][r];
+  // acc[r] = Y[tile row 4*lq + r][sequence b0 + ln]
   L = min(max(L, 0), p.Lmax);
   const double pos = static_cast<double>(L - 1);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float mine = acc[r];
-    const float other = __shfl_xor(mine, 32);
-    const int m = 4 * lq + r;          // tile row
-    const int fi = i0 + (m & 7);       // frequency index
-    const double w = pow(p.theta, -2.0 * static_cast<double>(fi) / static_cast<double>(p.DG));
-    double sn, cs;
-    sincos(pos * w, &sn, &cs);
-    double outv;
-    int grow;
-    if (m < 8) {  // lower half: x_i cos - x_{i+D/2} sin
-      outv = static_cast<double>(mine) * cs - static_cast<double>(other) * sn;
-      grow = fi;
-    } else {      // upper half: x_{i+D/2} cos + x_i sin
-      outv = static_cast<double>(mine) * cs + static_cast<double>(other) * sn;
-      grow = half + fi;
+    const float other = __shfl_xor(mine, 32);  // rows m and m^8 sit in lanes l and l^32
+    const int m = 4 * lq + r;
+    const int fi = i0 + (m & 7);
+    float olo, ohi;
+    if (m < 8) {
+      rope_pair(pos, p.freqs.w[fi], mine, other, &olo, &ohi);
+      if (bvalid) p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + fi] = olo;
+    } else {
+      rope_pair(pos, p.freqs.w[fi], other, mine, &olo, &ohi);
+      if (bvalid) p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + half + fi] = ohi;
     }
-    if (bvalid) p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * p.DG + grow] = static_cast<float>(outv);
   }
 }
 
-struct LogitParams {
-  const float* q_gate;
+template <int D, int DG>
+__global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
+  __shared__ union {
+    float red[4][64][4];
+    CompressSmem<D, DG> cm;
+  } sm;
+  const int t = blockIdx.x;
+  if (t < p.n_query_wgs) {
+    query_tile<D, DG>(p, t, sm.red);
+    return;
+  }
+  const int c = t - p.n_query_wgs;
+  const int pair = c / p.max_new;
+  const int z = c - pair * p.max_new;
+  const int b = pair / p.Hkv;
+  const int h = pair - b * p.Hkv;
+  int L = p.seq_lens[b];
+  L = min(max(L, 0), p.Lmax);
+  int cl = p.kcomp_lens[b];
+  cl = min(max(cl, 0), p.NBmax);
+  const int j = cl + z;
+  if (j >= L / p.BS) return;  // uniform over the workgroup
+  const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j) * p.BS * p.st;
+  uint16_t* dst = p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j) * DG;
+  compress_block<D, DG>(sm.cm, keys, p.st, p.BS, p.w_k + static_cast<int64_t>(h) * DG * 3 * D,
+                        p.freqs, j, dst);
+}
+
+__global__ void commit_kernel(const int32_t* seq_lens, int32_t* kcomp_lens, int B, int BS, int Lmax,
+                              int NBmax, int max_new) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  kcomp_lens[b] = committed_count(seq_lens[b], kcomp_lens[b], BS, Lmax, NBmax, max_new);
+}
+
+// ------------------------------------------------------------------ gate
+
+constexpr int kGateThreads = 512;
+constexpr int kGateRows = 512;  // cache rows per prefetch pass
+
+struct GateParams {
+  const float* q_gate;          // [B, H_kv, d_gate]
   const uint16_t* kcomp;
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
-  float* logits;
+  float* logits_out;            // [B, H_kv, NBmax] or null
+  int32_t* block_idx;           // select when non-null
+  int32_t* num_selected;
+  int pending_new;              // entries appended this step, not yet counted
   int Hkv, BS, Lmax, NBmax;
+  int mode, topk, max_sel;
+  float log_tau;
   float inv_sqrt_dg;
 };
 
-constexpr int kLogitRowsPerWg = 256;
-
-// grid (B*H_kv, ceil(NBmax/256)), 256 threads.  LPR = DG/8 lanes read one
-// 16-byte piece each of a cache row; a wave covers 64/LPR rows per load.
+// One 512-thread workgroup per (sequence, KV head): its cache rows are all
+// requested at once (16-byte pieces, DG/8 lanes per row), dotted with the
+// gate query, and -- in the fused step -- selected on by its first wave
+// without leaving LDS.
 template <int DG>
-__global__ __launch_bounds__(256) void logits_kernel(LogitParams p) {
-  constexpr int LPR = DG / 8;
-  constexpr int RPI = 64 / LPR;                    // rows per wave load
-  constexpr int ITER = kLogitRowsPerWg / 4 / RPI;  // loads per lane
+__global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
+  constexpr int LPR = DG / 8;                    // lanes per cache row
+  constexpr int RPI = 64 / LPR;                  // rows per wave load
+  constexpr int RPL = kGateThreads / 64 * RPI;   // rows per workgroup load
+  constexpr int NL = kGateRows / RPL;            // loads per lane per pass
+
+  extern __shared__ uint32_t s_keys[];           // NBmax logits (float bits)
+  __shared__ int s_hist[256];
+
   const int pair = blockIdx.x;
   const int b = pair / p.Hkv;
   const int tid = threadIdx.x;
@@ -114,72 +215,138 @@ __global__ __launch_bounds__(256) void logits_kernel(LogitParams p) {
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.Lmax);
   int nc = p.kcomp_lens[b];
-  nc = min(max(nc, 0), p.NBmax);
-  nc = min(nc, L / p.BS);
+  nc = min(min(max(nc, 0), p.NBmax) + p.pending_new, L / p.BS);  // scored blocks
 
-  float qv[8];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(p.q_gate + static_cast<int64_t>(pair) * DG + 8 * c);
-    const float4 a = qp[0], bb = qp[1];
-    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
-    qv[4] = bb.x; qv[5] = bb.y; qv[6] = bb.z; qv[7] = bb.w;
-  }
-  const int jbase = blockIdx.y * kLogitRowsPerWg + w * (kLogitRowsPerWg / 4) + rsub;
   const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 8 * c;
+  float* lo = p.logits_out ? p.logits_out + static_cast<int64_t>(pair) * p.NBmax : nullptr;
+  const int passes = max(1, (nc + kGateRows - 1) / kGateRows);
+  float qv[8];
+  for (int pass = 0; pass < passes; ++pass) {
+    const int base = pass * kGateRows;
+    uint4 kv[NL];
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+      const int j = base + it * RPL + w * RPI + rsub;
+      kv[it] = (j < nc) ? ld16(kc + static_cast<int64_t>(j) * DG) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (pass == 0) {  // the gate query, while the first rows are in flight
+      const float4* qp = reinterpret_cast<const float4*>(p.q_gate + static_cast<int64_t>(pair) * DG + 8 * c);
+      const float4 a = qp[0], bb = qp[1];
+      qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
+      qv[4] = bb.x; qv[5] = bb.y; qv[6] = bb.z; qv[7] = bb.w;
+    }
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+      const int j = base + it * RPL + w * RPI + rsub;
+      const float zj = logit_dot<DG>(qv, kv[it]) * p.inv_sqrt_dg;
+      if (c == 0 && j < p.NBmax) {
+        if (j < nc) s_keys[j] = __float_as_uint(zj);
+        if (lo != nullptr) lo[j] = (j < nc) ? zj : -INFINITY;
+      }
+    }
+  }
+  if (lo != nullptr)  // rows past the passes walked above
+    for (int j = passes * kGateRows + tid; j < p.NBmax; j += kGateThreads) lo[j] = -INFINITY;
+  if (p.block_idx == nullptr) return;
+  __syncthreads();
+  if (w != 0) return;
+  select_blocks_wave(s_keys, s_hist, nc, (L + p.BS - 1) / p.BS, p.mode, p.topk, p.log_tau,
+                     p.max_sel, p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
+                     p.num_selected + pair);
+}
 
-  uint4 kv[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int j = jbase + it * RPI;
-    kv[it] = (j < nc) ? ld16(kc + static_cast<int64_t>(j) * DG) : make_uint4(0u, 0u, 0u, 0u);
-  }
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int j = jbase + it * RPI;
-    const uint4 u = kv[it];
-    float s = bf_lo(u.x) * qv[0];
-    s = fmaf(bf_hi(u.x), qv[1], s);
-    s = fmaf(bf_lo(u.y), qv[2], s);
-    s = fmaf(bf_hi(u.y), qv[3], s);
-    s = fmaf(bf_lo(u.z), qv[4], s);
-    s = fmaf(bf_hi(u.z), qv[5], s);
-    s = fmaf(bf_lo(u.w), qv[6], s);
-    s = fmaf(bf_hi(u.w), qv[7], s);
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-    if (c == 0 && j < p.NBmax)
-      p.logits[static_cast<int64_t>(pair) * p.NBmax + j] = (j < nc) ? s * p.inv_sqrt_dg : -INFINITY;
-  }
+template <int D, int DG>
+void launch_prep_t(const PrepParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((prep_kernel<D, DG>), dim3(grid), dim3(256), 0, s, p);
 }
 
 }  // namespace
 
-int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
+float log_threshold(float tau);
+
+int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
+  PrepParams p{};
+  p.q_nope = a.q_nope;
+  p.w_q = a.w_q;
+  p.q_gate = a.q_gate;
+  p.n_query_wgs = a.q_gate ? d.num_kv_heads * (d.d_gate / 16) * ((d.batch + 15) / 16) : 0;
+  p.k_nope = a.k_nope;
+  p.w_k = a.w_k;
+  p.kcomp_lens = a.kcomp_lens;
+  p.kcomp = a.kcomp;
+  p.max_new = a.max_new_blocks;
+  p.seq_lens = a.seq_lens;
+  p.sb = d.kv_stride_b;
+  p.sh = d.kv_stride_h;
+  p.st = d.kv_stride_t;
+  p.B = d.batch;
+  p.Hq = d.num_q_heads;
+  p.Hkv = d.num_kv_heads;
+  p.G = d.num_q_heads / d.num_kv_heads;
+  p.BS = d.block_size;
+  p.Lmax = d.max_seq_len;
+  p.NBmax = static_cast<int>(nb_max(&d));
+  p.freqs = make_freqs(d.d_gate, a.theta);
+  const int64_t cache_wgs = (a.kcomp != nullptr && a.max_new_blocks > 0)
+                                ? static_cast<int64_t>(d.batch) * d.num_kv_heads * a.max_new_blocks
+                                : 0;
+  const int64_t grid = p.n_query_wgs + cache_wgs;
+  if (grid > 0x7fffffff) {
+    set_error("gate prep grid too large");
+    return SEER_ERR_UNSUPPORTED;
+  }
+  if (grid == 0) return SEER_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = d.num_q_heads / d.num_kv_heads;
-  QgateParams qp{a.q_nope, a.w_q, a.seq_lens, a.q_gate, d.batch, d.num_q_heads, d.num_kv_heads,
-                 G, d.head_dim, d.d_gate, d.max_seq_len, a.theta};
-  dim3 qgrid(d.num_kv_heads, d.d_gate / 16, (d.batch + 15) / 16);
-  hipLaunchKernelGGL(qgate_kernel, qgrid, dim3(64), 0, s, qp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error(std::string("gate query launch: ") + hipGetErrorString(e));
-    return SEER_ERR_HIP;
+  const int key = (d.head_dim == 128 ? 2 : 0) | (d.d_gate == 128 ? 1 : 0);
+  switch (key) {
+    case 0: launch_prep_t<64, 64>(p, static_cast<int>(grid), s); break;
+    case 1: launch_prep_t<64, 128>(p, static_cast<int>(grid), s); break;
+    case 2: launch_prep_t<128, 64>(p, static_cast<int>(grid), s); break;
+    default: launch_prep_t<128, 128>(p, static_cast<int>(grid), s); break;
   }
-  const int nbm = static_cast<int>(nb_max(&d));
-  LogitParams lp{a.q_gate, a.kcomp, a.kcomp_lens, a.seq_lens, a.logits, d.num_kv_heads,
-                 d.block_size, d.max_seq_len, nbm, static_cast<float>(1.0 / std::sqrt(double(d.d_gate)))};
-  dim3 lgrid(d.batch * d.num_kv_heads, (nbm + kLogitRowsPerWg - 1) / kLogitRowsPerWg);
+  return check_launch("gate prep launch");
+}
+
+int launch_commit(const seer_dims& d, const int32_t* seq_lens, int32_t* kcomp_lens, int max_new,
+                  void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(commit_kernel, dim3((d.batch + 255) / 256), dim3(256), 0, s, seq_lens,
+                     kcomp_lens, d.batch, d.block_size, d.max_seq_len,
+                     static_cast<int>(nb_max(&d)), max_new);
+  return check_launch("kcomp commit launch");
+}
+
+int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
+  GateParams p{};
+  p.q_gate = a.q_gate;
+  p.kcomp = a.kcomp;
+  p.kcomp_lens = a.kcomp_lens;
+  p.seq_lens = a.seq_lens;
+  p.logits_out = a.logits_out;
+  p.block_idx = a.block_idx;
+  p.num_selected = a.num_selected;
+  p.pending_new = a.pending_new;
+  p.Hkv = d.num_kv_heads;
+  p.BS = d.block_size;
+  p.Lmax = d.max_seq_len;
+  p.NBmax = static_cast<int>(nb_max(&d));
+  p.mode = a.mode;
+  p.topk = a.topk;
+  p.max_sel = a.max_selected;
+  p.log_tau = log_threshold(a.tau);
+  p.inv_sqrt_dg = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d_gate)));
+  const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads;
+  if (grid > 0x7fffffff) {
+    set_error("gate grid too large");
+    return SEER_ERR_UNSUPPORTED;
+  }
+  const size_t lds = static_cast<size_t>(p.NBmax) * sizeof(uint32_t);
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.d_gate == 128)
-    hipLaunchKernelGGL(logits_kernel<128>, lgrid, dim3(256), 0, s, lp);
+    hipLaunchKernelGGL(gate_kernel<128>, dim3(grid), dim3(kGateThreads), lds, s, p);
   else
-    hipLaunchKernelGGL(logits_kernel<64>, lgrid, dim3(256), 0, s, lp);
-  e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error(std::string("gate logits launch: ") + hipGetErrorString(e));
-    return SEER_ERR_HIP;
-  }
-  return SEER_OK;
+    hipLaunchKernelGGL(gate_kernel<64>, dim3(grid), dim3(kGateThreads), lds, s, p);
+  return check_launch("gate launch");
 }
 
 }  // namespace seer

@@ -1,0 +1,142 @@
+// Device pieces of the AttnGate shared by the gate kernels and the fused
+// decode step, for gfx950 (MI355X).
+//
+// [CP Knowl 1, Knowl 2] (chapterpal page "SeerAttention-R: Sparse Attention
+// Adaptation for Long Reasoning"):
+//   K branch: max / min / average pooling of each non-overlapping b-token
+//   block of pre-RoPE keys, concatenated (3d values), mapped by W_k
+//   (d_gate x 3d), then RoPE at the block's first-token position.
+//   Q branch: the g query heads of a GQA group concatenated (g*d values),
+//   mapped by W_q (d_gate x g*d), then RoPE at the query position.
+// [CP Knowl 5]: the K Compression Cache stores K_gate, one entry per
+// complete block.
+#pragma once
+
+#include "seer_device.hpp"
+
+namespace seer {
+
+// RoPE frequencies theta^(-2i/d_gate), i < d_gate/2, formed on the host in
+// float64 and passed by value.
+struct RopeFreqs {
+  double w[64];
+};
+
+// Rotate-half RoPE of the pair (lo, hi) = (x_i, x_{i+D/2}) at angle pos*w,
+// angles and products in float64.  The angle (up to ~1e5 rad) is first
+// reduced to [-pi, pi] with a two-part 2*pi (Cody-Waite): each fma forms its
+// product exactly and rounds once, so the reduced angle is good to ~1e-15
+// rad, and sincos then runs on a small argument.
+__device__ __forceinline__ void rope_pair(double pos, double w, float lo, float hi, float* out_lo,
+                                          float* out_hi) {
+  constexpr double kTwoPiHi = 6.283185307179586;             // 2*pi rounded to double
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;         // 2*pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189535;
+  const double a = pos * w;
+  const double k = rint(a * kInvTwoPi);
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
+  double sn, cs;
+  sincos(r, &sn, &cs);
+  *out_lo = static_cast<float>(static_cast<double>(lo) * cs - static_cast<double>(hi) * sn);
+  *out_hi = static_cast<float>(static_cast<double>(hi) * cs + static_cast<double>(lo) * sn);
+}
+
+// Shared-memory scratch of one cache-entry computation.
+template <int D, int DG>
+struct CompressSmem {
+  static constexpr int CP = D / 2;      // channel pairs
+  static constexpr int NTG = 256 / CP;  // token groups
+  float red[3][NTG][D];
+  float u[3 * D];
+  float v[DG];
+};
+
+// One K Compression Cache entry (block j of pair (b, h)) computed by the
+// first 256 threads of the workgroup; the caller provides the barrier
+// discipline (every thread of the workgroup must call this).
+//   pooling: each (channel pair, token group) thread reduces a strided set
+//   of tokens, then threads < D fold the groups in a fixed order;
+//   GEMV: wave w of the 256 handles rows w, w+4, ...; lanes split the 3d
+//   columns and reduce by butterflies;
+//   RoPE at position j*b in float64, bf16 store (round to nearest even).
+template <int D, int DG>
+__device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* row 0 of block */,
+                               int64_t st, int BS, const uint16_t* w_k_h, const RopeFreqs& freqs,
+                               int j, uint16_t* dst) {
+  constexpr int CP = CompressSmem<D, DG>::CP;
+  constexpr int NTG = CompressSmem<D, DG>::NTG;
+  const int tid = threadIdx.x;
+  if (tid < 256) {
+    const int cp = tid % CP;
+    const int tg = tid / CP;
+    const uint16_t* base = keys + 2 * cp;
+    float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY, s0 = 0.f, s1 = 0.f;
+    for (int t = tg; t < BS; t += NTG) {
+      const uint32_t wv = *reinterpret_cast<const uint32_t*>(base + t * st);
+      const float a = bf_lo(wv), bb = bf_hi(wv);
+      mx0 = fmaxf(mx0, a); mn0 = fminf(mn0, a); s0 += a;
+      mx1 = fmaxf(mx1, bb); mn1 = fminf(mn1, bb); s1 += bb;
+    }
+    sm.red[0][tg][2 * cp] = mx0; sm.red[0][tg][2 * cp + 1] = mx1;
+    sm.red[1][tg][2 * cp] = mn0; sm.red[1][tg][2 * cp + 1] = mn1;
+    sm.red[2][tg][2 * cp] = s0;  sm.red[2][tg][2 * cp + 1] = s1;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float mx = -INFINITY, mn = INFINITY, sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < NTG; ++g) {
+      mx = fmaxf(mx, sm.red[0][g][tid]);
+      mn = fminf(mn, sm.red[1][g][tid]);
+      sum += sm.red[2][g][tid];
+    }
+    sm.u[tid] = mx;
+    sm.u[D + tid] = mn;
+    sm.u[2 * D + tid] = sum / static_cast<float>(BS);
+  }
+  __syncthreads();
+  if (tid < 256) {
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    for (int r = w; r < DG; r += 4) {
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(w_k_h + static_cast<int64_t>(r) * 3 * D);
+      float acc = 0.f;
+      for (int q2 = lane; q2 < 3 * D / 2; q2 += 64) {
+        const uint32_t wv = row[q2];
+        acc = fmaf(bf_lo(wv), sm.u[2 * q2], acc);
+        acc = fmaf(bf_hi(wv), sm.u[2 * q2 + 1], acc);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+      if (lane == 0) sm.v[r] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < DG / 2) {
+    float olo, ohi;
+    rope_pair(static_cast<double>(j) * BS, freqs.w[tid], sm.v[tid], sm.v[tid + DG / 2], &olo, &ohi);
+    dst[tid] = f2bf(olo);
+    dst[tid + DG / 2] = f2bf(ohi);
+  }
+}
+
+// Dot product of a gate query (8 float values per lane, lanes of a row
+// group of DG/8 lanes) with one bf16 cache row piece, reduced over the row
+// group by butterflies; every lane of the group ends with the sum.
+template <int DG>
+__device__ __forceinline__ float logit_dot(const float (&qv)[8], uint4 u) {
+  constexpr int LPR = DG / 8;
+  float s = bf_lo(u.x) * qv[0];
+  s = fmaf(bf_hi(u.x), qv[1], s);
+  s = fmaf(bf_lo(u.y), qv[2], s);
+  s = fmaf(bf_hi(u.y), qv[3], s);
+  s = fmaf(bf_lo(u.z), qv[4], s);
+  s = fmaf(bf_hi(u.z), qv[5], s);
+  s = fmaf(bf_lo(u.w), qv[6], s);
+  s = fmaf(bf_hi(u.w), qv[7], s);
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
+}  // namespace seer

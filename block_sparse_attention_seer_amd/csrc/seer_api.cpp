@@ -48,6 +48,29 @@ bool tuning_merge_inline() {
   return v;
 }
 
+int check_select_args(const seer_dims* dims, int32_t mode, int32_t topk_blocks, float threshold,
+                      int32_t max_selected) {
+  const int64_t nbm = seer::nb_max(dims);
+  if (nbm > seer::kMaxNBSelect)
+    return fail(SEER_ERR_UNSUPPORTED, "select needs ceil(max_seq_len / block_size) <= 8192");
+  if (mode == SEER_SELECT_TOPK) {
+    if (topk_blocks < 0) return fail(SEER_ERR_INVALID_ARG, "topk_blocks must be >= 0");
+    const int64_t need = std::min<int64_t>(static_cast<int64_t>(topk_blocks) + 1, nbm);
+    if (max_selected < need)
+      return fail(SEER_ERR_INVALID_ARG, "max_selected must be >= min(topk_blocks + 1, NBmax)");
+  } else if (mode == SEER_SELECT_THRESHOLD) {
+    if (!(threshold >= 0.0f && threshold <= 1.0f))
+      return fail(SEER_ERR_INVALID_ARG, "threshold must be in [0, 1]");
+    if (max_selected < nbm)
+      return fail(SEER_ERR_INVALID_ARG, "threshold mode needs max_selected >= NBmax");
+  } else {
+    return fail(SEER_ERR_INVALID_ARG, "mode must be SEER_SELECT_TOPK or SEER_SELECT_THRESHOLD");
+  }
+  if (max_selected < 1 || max_selected > nbm)
+    return fail(SEER_ERR_INVALID_ARG, "max_selected must be in [1, NBmax]");
+  return SEER_OK;
+}
+
 int resolve_split(const seer_dims* d, int max_blocks, int num_split, int* out) {
   if (num_split < 0 || num_split > seer::kMaxSplit)
     return fail(SEER_ERR_INVALID_ARG, "num_split must be in [0, 128]");
@@ -79,8 +102,17 @@ int seer_kcomp_update(const seer_dims* dims, const uint16_t* k_nope, const uint1
   if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
     return fail(SEER_ERR_INVALID_ARG, "rope_theta must be positive and finite");
   if (max_new_blocks > seer::nb_max(dims)) max_new_blocks = static_cast<int32_t>(seer::nb_max(dims));
-  seer::KcompArgs a{k_nope, w_k, seq_lens, kcomp_lens, kcomp, max_new_blocks, rope_theta};
-  return seer::launch_kcomp(*dims, a, stream);
+  seer::PrepArgs a{};
+  a.k_nope = k_nope;
+  a.w_k = w_k;
+  a.kcomp_lens = kcomp_lens;
+  a.kcomp = kcomp;
+  a.max_new_blocks = max_new_blocks;
+  a.seq_lens = seq_lens;
+  a.theta = rope_theta;
+  int rc = seer::launch_prep(*dims, a, stream);
+  if (rc != SEER_OK) return rc;
+  return seer::launch_commit(*dims, seq_lens, kcomp_lens, max_new_blocks, stream);
 }
 
 size_t seer_gate_workspace_bytes(const seer_dims* dims) {
@@ -105,9 +137,22 @@ int seer_gate_scores(const seer_dims* dims, const uint16_t* q_nope, const uint16
   if (workspace == nullptr || workspace_bytes < seer::gate_workspace_bytes(dims))
     return fail(SEER_ERR_WORKSPACE, "gate workspace missing or smaller than seer_gate_workspace_bytes()");
   SEER_CHECK(check_ptr(workspace, 16, "workspace", &why_));
-  seer::GateArgs a{q_nope, w_q, kcomp, kcomp_lens, seq_lens, rope_theta,
-                   static_cast<float*>(workspace), logits};
-  return seer::launch_gate(*dims, a, stream);
+  float* q_gate = static_cast<float*>(workspace);
+  seer::PrepArgs pa{};
+  pa.q_nope = q_nope;
+  pa.w_q = w_q;
+  pa.q_gate = q_gate;
+  pa.seq_lens = seq_lens;
+  pa.theta = rope_theta;
+  int rc = seer::launch_prep(*dims, pa, stream);
+  if (rc != SEER_OK) return rc;
+  seer::GateArgs ga{};
+  ga.q_gate = q_gate;
+  ga.kcomp = kcomp;
+  ga.kcomp_lens = kcomp_lens;
+  ga.seq_lens = seq_lens;
+  ga.logits_out = logits;
+  return seer::launch_gate(*dims, ga, stream);
 }
 
 int seer_select_blocks(const seer_dims* dims, const float* logits, const int32_t* kcomp_lens,
@@ -120,24 +165,10 @@ int seer_select_blocks(const seer_dims* dims, const float* logits, const int32_t
   SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
   SEER_CHECK(check_ptr(block_idx, 4, "block_idx", &why_));
   SEER_CHECK(check_ptr(num_selected, 4, "num_selected", &why_));
-  const int64_t nbm = seer::nb_max(dims);
-  if (nbm > seer::kMaxNBSelect)
-    return fail(SEER_ERR_UNSUPPORTED, "select needs ceil(max_seq_len / block_size) <= 8192");
-  if (mode == SEER_SELECT_TOPK) {
-    if (topk_blocks < 0) return fail(SEER_ERR_INVALID_ARG, "topk_blocks must be >= 0");
-    const int64_t need = std::min<int64_t>(static_cast<int64_t>(topk_blocks) + 1, nbm);
-    if (max_selected < need)
-      return fail(SEER_ERR_INVALID_ARG, "max_selected must be >= min(topk_blocks + 1, NBmax)");
-  } else if (mode == SEER_SELECT_THRESHOLD) {
-    if (!(threshold >= 0.0f && threshold <= 1.0f))
-      return fail(SEER_ERR_INVALID_ARG, "threshold must be in [0, 1]");
-    if (max_selected < nbm)
-      return fail(SEER_ERR_INVALID_ARG, "threshold mode needs max_selected >= NBmax");
-  } else {
-    return fail(SEER_ERR_INVALID_ARG, "mode must be SEER_SELECT_TOPK or SEER_SELECT_THRESHOLD");
+  {
+    const int rc = check_select_args(dims, mode, topk_blocks, threshold, max_selected);
+    if (rc != SEER_OK) return rc;
   }
-  if (max_selected < 1 || max_selected > nbm)
-    return fail(SEER_ERR_INVALID_ARG, "max_selected must be in [1, NBmax]");
   seer::SelectArgs a{logits, kcomp_lens, seq_lens, mode, topk_blocks, threshold,
                      max_selected, block_idx, num_selected};
   return seer::launch_select(*dims, a, stream);
@@ -169,7 +200,8 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
                          const uint16_t* v, const int32_t* seq_lens, const int32_t* block_idx,
                          const int32_t* num_selected, int32_t max_blocks, float scale,
                          int32_t num_split, void* workspace, size_t workspace_bytes,
-                         uint16_t* out, float* lse, void* stream) {
+                         uint16_t* out, float* lse, void* stream,
+                         int32_t* commit_lens = nullptr, int commit_max_new = 0) {
   SEER_CHECK(check_dims(dims, &why_));
   SEER_CHECK(check_ptr(q, 16, "q", &why_));
   SEER_CHECK(check_ptr(k, 16, "k_cache", &why_));
@@ -192,7 +224,8 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
     SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
   }
   seer::DecodeArgs a{q, k, v, seq_lens, block_idx, num_selected, max_blocks, scale, s,
-                     tuning_waves(), tuning_merge_inline(), workspace, out, lse};
+                     tuning_waves(), tuning_merge_inline(), workspace, out, lse,
+                     commit_lens, commit_max_new};
   return seer::launch_decode(*dims, a, stream);
 }
 
@@ -216,6 +249,95 @@ int seer_dense_decode(const seer_dims* dims, const uint16_t* q, const uint16_t* 
   return decode_common(dims, q, k_cache, v_cache, seq_lens, nullptr, nullptr,
                        static_cast<int32_t>(seer::nb_max(dims)), scale, num_split, workspace,
                        workspace_bytes, out, lse, stream);
+}
+
+int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16_t* q,
+                     const uint16_t* k_nope, const uint16_t* k_cache, const uint16_t* v_cache,
+                     const uint16_t* w_q, const uint16_t* w_k, const int32_t* seq_lens,
+                     int32_t* kcomp_lens, uint16_t* kcomp, int32_t max_new_blocks,
+                     double rope_theta, int32_t mode, int32_t topk_blocks, float threshold,
+                     int32_t max_selected, int32_t* block_idx, int32_t* num_selected,
+                     float* logits, float scale, int32_t num_split, void* workspace,
+                     size_t workspace_bytes, uint16_t* out, float* lse, void* stream) {
+  SEER_CHECK(check_dims(dims, &why_));
+  SEER_CHECK(check_ptr(q_nope, 16, "q_nope", &why_));
+  SEER_CHECK(check_ptr(q, 16, "q", &why_));
+  SEER_CHECK(check_ptr(k_nope, 16, "k_nope", &why_));
+  SEER_CHECK(check_ptr(k_cache, 16, "k_cache", &why_));
+  SEER_CHECK(check_ptr(v_cache, 16, "v_cache", &why_));
+  SEER_CHECK(check_ptr(w_q, 16, "w_q", &why_));
+  SEER_CHECK(check_ptr(w_k, 16, "w_k", &why_));
+  SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
+  SEER_CHECK(check_ptr(kcomp_lens, 4, "kcomp_lens", &why_));
+  SEER_CHECK(check_ptr(kcomp, 16, "kcomp", &why_));
+  SEER_CHECK(check_ptr(block_idx, 4, "block_idx", &why_));
+  SEER_CHECK(check_ptr(num_selected, 4, "num_selected", &why_));
+  if (logits != nullptr) SEER_CHECK(check_ptr(logits, 4, "logits", &why_));
+  SEER_CHECK(check_ptr(out, 16, "out", &why_));
+  if (lse != nullptr) SEER_CHECK(check_ptr(lse, 4, "lse", &why_));
+  if (max_new_blocks < 0) return fail(SEER_ERR_INVALID_ARG, "max_new_blocks must be >= 0");
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(SEER_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+  if (!std::isfinite(scale)) return fail(SEER_ERR_INVALID_ARG, "scale must be finite");
+  {
+    const int rc = check_select_args(dims, mode, topk_blocks, threshold, max_selected);
+    if (rc != SEER_OK) return rc;
+  }
+  int s = 0;
+  {
+    const int rc = resolve_split(dims, max_selected, num_split, &s);
+    if (rc != SEER_OK) return rc;
+  }
+  const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
+  const size_t dec_bytes = seer::decode_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
+                                                        dims->head_dim);
+  if (workspace == nullptr || workspace_bytes < dec_bytes + seer::step_gate_bytes(dims))
+    return fail(SEER_ERR_WORKSPACE, "workspace missing or smaller than seer_decode_step_workspace_bytes()");
+  SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
+  if (max_new_blocks > seer::nb_max(dims)) max_new_blocks = static_cast<int32_t>(seer::nb_max(dims));
+
+  // Launch 1: gate-query tiles plus the entries of newly completed blocks.
+  // Launch 2: logits and selection per (b, h), counting those entries.
+  // Launch 3: the sparse decode, which also commits them to kcomp_lens.
+  float* q_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec_bytes);
+  seer::PrepArgs pa{};
+  pa.q_nope = q_nope;
+  pa.w_q = w_q;
+  pa.q_gate = q_gate;
+  pa.k_nope = k_nope;
+  pa.w_k = w_k;
+  pa.kcomp_lens = kcomp_lens;
+  pa.kcomp = max_new_blocks > 0 ? kcomp : nullptr;
+  pa.max_new_blocks = max_new_blocks;
+  pa.seq_lens = seq_lens;
+  pa.theta = rope_theta;
+  int rc = seer::launch_prep(*dims, pa, stream);
+  if (rc != SEER_OK) return rc;
+  seer::GateArgs ga{};
+  ga.q_gate = q_gate;
+  ga.kcomp = kcomp;
+  ga.kcomp_lens = kcomp_lens;
+  ga.seq_lens = seq_lens;
+  ga.pending_new = max_new_blocks;
+  ga.logits_out = logits;
+  ga.block_idx = block_idx;
+  ga.num_selected = num_selected;
+  ga.mode = mode;
+  ga.topk = topk_blocks;
+  ga.max_selected = max_selected;
+  ga.tau = threshold;
+  rc = seer::launch_gate(*dims, ga, stream);
+  if (rc != SEER_OK) return rc;
+  return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,
+                       scale, s, workspace, dec_bytes, out, lse, stream,
+                       max_new_blocks > 0 ? kcomp_lens : nullptr, max_new_blocks);
+}
+
+size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selected,
+                                        int32_t num_split) {
+  std::string why;
+  if (check_dims(dims, &why) != SEER_OK || max_selected < 1) return 0;
+  return seer_decode_workspace_bytes(dims, max_selected, num_split) + seer::step_gate_bytes(dims);
 }
 
 }  // extern "C"

@@ -94,6 +94,10 @@ size_t gate_workspace_bytes(const seer_dims* d) {
   return static_cast<size_t>(d->batch) * d->num_kv_heads * d->d_gate * sizeof(float);
 }
 
+size_t step_gate_bytes(const seer_dims* d) {
+  return (gate_workspace_bytes(d) + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
+}
+
 size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim) {
   if (num_split <= 1) return 0;  // a single split writes the output directly
   size_t counters = static_cast<size_t>(pairs) * sizeof(int32_t);

@@ -51,4 +51,15 @@ __device__ __forceinline__ uint32_t float_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Number of K Compression Cache entries after an update that may append up
+// to max_new blocks: min(floor(L/b), c + max_new), never below the clamped
+// old count c.
+__device__ __forceinline__ int committed_count(int L, int c, int BS, int Lmax, int NBmax,
+                                               int max_new) {
+  L = min(max(L, 0), Lmax);
+  c = min(max(c, 0), NBmax);
+  const int nw = min(L / BS, c + max_new);
+  return nw > c ? nw : c;
+}
+
 }  // namespace seer

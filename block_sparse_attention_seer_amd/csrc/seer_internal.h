@@ -26,6 +26,8 @@ int check_ptr(const void* p, size_t align, const char* name, std::string* why);
 
 int64_t nb_max(const seer_dims* d);  // ceil(Lmax / b)
 size_t gate_workspace_bytes(const seer_dims* d);
+// Gate-query scratch of the fused step, rounded up to 256 bytes.
+size_t step_gate_bytes(const seer_dims* d);
 // Workspace of the decode kernel for `pairs` (b, h) pairs, `num_split`
 // splits and group size g: the per-split lse and outputs.
 size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim);
@@ -37,26 +39,38 @@ const char* last_error();
 
 // ------------------------------------------------------ kernel launchers
 // Implemented in the .hip files.  Arguments were validated by the caller.
-struct KcompArgs {
-  const uint16_t* k_nope;
-  const uint16_t* w_k;
-  const int32_t* seq_lens;
-  int32_t* kcomp_lens;
-  uint16_t* kcomp;
-  int max_new_blocks;
-  double theta;
-};
-int launch_kcomp(const seer_dims& d, const KcompArgs& a, void* stream);
-
-struct GateArgs {
+// One launch for the gate-query tiles (when q_gate != nullptr) and the
+// cache-entry tasks (entries kcomp_lens[b] + z, z < max_new_blocks, of every
+// (b, h) whose block is complete; when kcomp != nullptr).
+struct PrepArgs {
   const uint16_t* q_nope;
   const uint16_t* w_q;
+  float* q_gate;  // [B, H_kv, d_gate] or nullptr
+  const uint16_t* k_nope;
+  const uint16_t* w_k;
+  const int32_t* kcomp_lens;
+  uint16_t* kcomp;  // or nullptr
+  int max_new_blocks;
+  const int32_t* seq_lens;
+  double theta;
+};
+int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream);
+int launch_commit(const seer_dims& d, const int32_t* seq_lens, int32_t* kcomp_lens, int max_new,
+                  void* stream);
+
+// Per-(b, h) block logits from the gate query, and the selection when
+// block_idx != nullptr.
+struct GateArgs {
+  const float* q_gate;
   const uint16_t* kcomp;
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
-  double theta;
-  float* q_gate;   // workspace [B, H_kv, d_gate]
-  float* logits;
+  int pending_new;         // entries appended this step and not yet counted
+  float* logits_out;       // or nullptr
+  int32_t* block_idx;      // selection when non-null
+  int32_t* num_selected;
+  int mode, topk, max_selected;
+  float tau;
 };
 int launch_gate(const seer_dims& d, const GateArgs& a, void* stream);
 
@@ -88,6 +102,8 @@ struct DecodeArgs {
   void* workspace;
   uint16_t* out;
   float* lse;
+  int32_t* commit_lens;         // fused step: raise kcomp_lens here (or nullptr)
+  int commit_max_new;
 };
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
 

@@ -11,6 +11,7 @@
  * One decode step of one attention layer is
  *   seer_kcomp_update  -> seer_gate_scores -> seer_select_blocks
  *   -> seer_sparse_decode            (seer_dense_decode is the full baseline)
+ * or the same four stages fused into fewer launches by seer_decode_step.
  *
  * Conventions shared by every call
  *   - "bf16" buffers hold raw bfloat16 bit patterns (uint16_t).
@@ -113,7 +114,7 @@ typedef struct seer_dims {
  *   kcomp       [B, H_kv, NBmax, d_gate] bf16 (entries written).
  *   max_new_blocks >= 1; rope_theta > 0 (RoPE base, e.g. 10000).
  * Launches two kernels; the second raises kcomp_lens after all entries are
- * written.
+ * written.  An out-of-range kcomp_lens[b] is clamped to [0, NBmax].
  */
 int seer_kcomp_update(const seer_dims* dims, const uint16_t* k_nope,
                       const uint16_t* w_k, const int32_t* seq_lens,
@@ -237,6 +238,47 @@ int seer_dense_decode(const seer_dims* dims, const uint16_t* q,
                       const int32_t* seq_lens, float scale, int32_t num_split,
                       void* workspace, size_t workspace_bytes, uint16_t* out,
                       float* lse, void* stream);
+
+/*
+ * seer_decode_step -- one whole decode step of one layer in three launches,
+ * with the same results as seer_kcomp_update (with max_new_blocks), then
+ * seer_gate_scores, seer_select_blocks and seer_sparse_decode, in that order
+ * ([CP Knowl 5]: cache update, gating and binarisation; [CP Knowl 6]: the
+ * block-sparse decode).
+ *
+ * Launch 1 forms the gate queries (one GEMM per KV head) and the cache
+ * entries of blocks completed since the last update; launch 2 scores and
+ * selects the blocks of each (b, h) in one workgroup, counting those new
+ * entries; launch 3 is the sparse decode with its split merge, whose first
+ * workgroup also raises kcomp_lens -- so kcomp_lens keeps its old value
+ * until then and nothing else may read it in between.
+ *
+ *   q_nope, q        [B, H_q, d] pre-/post-RoPE queries (may alias).
+ *   k_nope, k_cache, v_cache  caches (layout above; k_nope may alias k_cache).
+ *   w_q, w_k         gate weights.   seq_lens [B] includes the current token.
+ *   kcomp_lens, kcomp  the cache (updated in place).  max_new_blocks >= 0
+ *                    (0: no update, e.g. when the caller keeps it current).
+ *   mode, topk_blocks, threshold, max_selected  as seer_select_blocks.
+ *   block_idx, num_selected  the selection (outputs).
+ *   logits           [B, H_kv, NBmax] float32 block scores, or NULL to skip
+ *                    writing them.
+ *   scale, num_split as seer_sparse_decode.
+ *   workspace        >= seer_decode_step_workspace_bytes(dims, max_selected,
+ *                    num_split) bytes, 256-byte aligned: the decode workspace
+ *                    (zero before first use) followed by the gate queries.
+ *   out, lse         as seer_sparse_decode.
+ */
+size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selected,
+                                        int32_t num_split);
+int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16_t* q,
+                     const uint16_t* k_nope, const uint16_t* k_cache,
+                     const uint16_t* v_cache, const uint16_t* w_q, const uint16_t* w_k,
+                     const int32_t* seq_lens, int32_t* kcomp_lens, uint16_t* kcomp,
+                     int32_t max_new_blocks, double rope_theta, int32_t mode,
+                     int32_t topk_blocks, float threshold, int32_t max_selected,
+                     int32_t* block_idx, int32_t* num_selected, float* logits,
+                     float scale, int32_t num_split, void* workspace,
+                     size_t workspace_bytes, uint16_t* out, float* lse, void* stream);
 
 /* Host-only helpers. */
 const char* seer_status_string(int status);

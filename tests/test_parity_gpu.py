@@ -480,3 +480,72 @@ def test_binding_rejects_bad_shapes(S):
         S.seer_dense_decode(dims, q, k, k, seq, 0.1, 1, None, out)
     with pytest.raises(S.SeerError):
         S.seer_decode_num_split(dims, 4, 500)
+
+
+# ------------------------------------------------------------- fused step
+
+def _clone_state(st_from, st_to):
+    st_to.kcomp.copy_(st_from.kcomp)
+    st_to.kcomp_lens.copy_(st_from.kcomp_lens)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("tiny", dict(seq_len=1024)),
+    ("tiny", dict(seq_len=1000)),
+    ("tiny", dict(seq_len=37)),
+    ("qwen3_8b_layer", {}),
+    ("qwen3_14b_b16", dict(batch=4)),
+    ("threshold_b128", dict(batch=6, max_seq_len=20000, seq_len_range=(3000, 20000))),
+])
+def test_fused_step_equals_staged(S, name, overrides):
+    """seer_decode_step reproduces the four staged calls bit for bit."""
+    w = WORKLOADS[name].replace(**overrides)
+    say(f"fused vs staged {name} {overrides}")
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
+    a = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
+    b = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
+    seq = inp["seq_lens"]
+    a.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    _clone_state(a, b)
+    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    a.step(*args)
+    b.fused_step(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a.kcomp_lens, b.kcomp_lens)
+    assert torch.equal(a.kcomp, b.kcomp)
+    assert torch.equal(a.num_selected, b.num_selected)
+    assert torch.equal(a.block_idx, b.block_idx)
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.lse, b.lse)
+    assert torch.equal(a.logits, b.logits)
+    # the fused workspace's counters are left at zero
+    assert int(b.step_ws[: w.batch * w.num_kv_heads].view(torch.int32).abs().sum()) == 0
+    # one pair against the oracle as well
+    _check_pair(w, inp, b, w.batch - 1, w.num_kv_heads - 1, f"fused {name}")
+
+
+def test_fused_pipeline_steps_match_oracle(S):
+    """Consecutive fused steps with appends keep the cache and outputs right."""
+    from workloads import append_token
+    w = WORKLOADS["pipeline_128k"].replace(batch=3, max_seq_len=4096, seq_len_range=(300, 700),
+                                           steps=70)
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    gen = torch.Generator(device=DEV).manual_seed(78)
+    for step in range(w.steps):
+        append_token(inp, gen)
+        st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+                      inp["seq_lens"])
+        if step % 23 == 0 or step == w.steps - 1:
+            torch.cuda.synchronize()
+            say(f"fused pipeline step {step}")
+            assert st.kcomp_lens.cpu().tolist() == [int(L) // 64 for L in inp["seq_lens"].cpu()]
+            for b in range(w.batch):
+                for h in (0, w.num_kv_heads - 1):
+                    _check_pair(w, inp, st, b, h, f"fused pipeline step={step} b={b} h={h}")
