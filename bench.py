@@ -120,7 +120,7 @@ def main() -> int:
         S.seer_decode_step(dims, inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
                            inp["w_k"], inp["seq_lens"], st.kcomp_lens, st.kcomp, 1, w.theta, mode,
                            w.topk_blocks, w.tau, st.max_selected, st.block_idx, st.num_selected,
-                           st.logits, scale, st.num_split, st.step_ws, st.out, st.lse)
+                           None, scale, st.num_split, st.step_ws, st.out, st.lse)
 
     def decode_only(r):
         inp, st = reps[r]

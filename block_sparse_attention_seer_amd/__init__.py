@@ -309,7 +309,8 @@ def seer_decode_step(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w
     _need(kcomp, "kcomp", torch.bfloat16, (B, Hkv, dims.nb_max, dg), dev)
     _need(block_idx, "block_idx", torch.int32, (B, Hkv, max_selected), dev)
     _need(num_selected, "num_selected", torch.int32, (B, Hkv), dev)
-    _need(logits, "logits", torch.float32, (B, Hkv, dims.nb_max), dev)
+    if logits is not None:  # optional: the selection reads the logits from LDS
+        _need(logits, "logits", torch.float32, (B, Hkv, dims.nb_max), dev)
     wp, wn = _ws(workspace, dev)
     _check(lib().seer_decode_step(
         ctypes.byref(dims), _ptr(q_nope), _ptr(q), _ptr(k_nope), _ptr(k_cache), _ptr(v_cache),
@@ -387,14 +388,16 @@ class DecodeStep:
         return self.out, self.lse
 
     def fused_step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
-                   scale: Optional[float] = None, max_new_blocks: int = 1):
-        """The same step through seer_decode_step (fewer launches)."""
+                   scale: Optional[float] = None, max_new_blocks: int = 1,
+                   keep_logits: bool = True):
+        """The same step through seer_decode_step (fewer launches); with
+        keep_logits=False the logits are not written out."""
         d = self.dims
         if scale is None:
             scale = 1.0 / math.sqrt(d.head_dim)
         seer_decode_step(d, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
                          self.kcomp_lens, self.kcomp, max_new_blocks, self.rope_theta, self.mode,
                          self.topk_blocks, self.threshold, self.max_selected, self.block_idx,
-                         self.num_selected, self.logits, scale, self.num_split, self.step_ws,
-                         self.out, self.lse)
+                         self.num_selected, self.logits if keep_logits else None, scale,
+                         self.num_split, self.step_ws, self.out, self.lse)
         return self.out, self.lse

@@ -124,14 +124,12 @@ __device__ void query_tile(const PrepParams& p, int t, float (*red)[64][4]) {
     const float other = __shfl_xor(mine, 32);  // rows m and m^8 sit in lanes l and l^32
     const int m = 4 * lq + r;
     const int fi = i0 + (m & 7);
+    const bool first = m < 8;  // this lane holds x_fi (else x_{fi+DG/2})
     float olo, ohi;
-    if (m < 8) {
-      rope_pair(pos, p.freqs.w[fi], mine, other, &olo, &ohi);
-      if (bvalid) p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + fi] = olo;
-    } else {
-      rope_pair(pos, p.freqs.w[fi], other, mine, &olo, &ohi);
-      if (bvalid) p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + half + fi] = ohi;
-    }
+    rope_pair(pos, p.freqs.w[fi], first ? mine : other, first ? other : mine, &olo, &ohi);
+    if (bvalid)
+      p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + (first ? fi : half + fi)] =
+          first ? olo : ohi;
   }
 }
 
@@ -192,8 +190,8 @@ struct GateParams {
 
 // One 512-thread workgroup per (sequence, KV head): its cache rows are all
 // requested at once (16-byte pieces, DG/8 lanes per row), dotted with the
-// gate query, and -- in the fused step -- selected on by its first wave
-// without leaving LDS.
+// gate query, and -- in the fused step -- selected on by the whole
+// workgroup without leaving LDS.
 template <int DG>
 __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   constexpr int LPR = DG / 8;                    // lanes per cache row
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   constexpr int NL = kGateRows / RPL;            // loads per lane per pass
 
   extern __shared__ uint32_t s_keys[];           // NBmax logits (float bits)
-  __shared__ int s_hist[256];
+  __shared__ SelectSmem s_sel;
 
   const int pair = blockIdx.x;
   const int b = pair / p.Hkv;
@@ -216,6 +214,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   L = min(max(L, 0), p.Lmax);
   int nc = p.kcomp_lens[b];
   nc = min(min(max(nc, 0), p.NBmax) + p.pending_new, L / p.BS);  // scored blocks
+  if (tid < 256) s_sel.hist[tid] = 0;
 
   const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 8 * c;
   float* lo = p.logits_out ? p.logits_out + static_cast<int64_t>(pair) * p.NBmax : nullptr;
@@ -249,10 +248,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
     for (int j = passes * kGateRows + tid; j < p.NBmax; j += kGateThreads) lo[j] = -INFINITY;
   if (p.block_idx == nullptr) return;
   __syncthreads();
-  if (w != 0) return;
-  select_blocks_wave(s_keys, s_hist, nc, (L + p.BS - 1) / p.BS, p.mode, p.topk, p.log_tau,
-                     p.max_sel, p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
-                     p.num_selected + pair);
+  select_blocks_wg<kGateThreads>(s_keys, s_sel, nc, (L + p.BS - 1) / p.BS, p.mode, p.topk,
+                                 p.log_tau, p.max_sel,
+                                 p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
+                                 p.num_selected + pair);
 }
 
 template <int D, int DG>

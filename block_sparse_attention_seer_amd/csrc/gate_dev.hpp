@@ -22,11 +22,14 @@ struct RopeFreqs {
   double w[64];
 };
 
-// Rotate-half RoPE of the pair (lo, hi) = (x_i, x_{i+D/2}) at angle pos*w,
-// angles and products in float64.  The angle (up to ~1e5 rad) is first
-// reduced to [-pi, pi] with a two-part 2*pi (Cody-Waite): each fma forms its
-// product exactly and rounds once, so the reduced angle is good to ~1e-15
-// rad, and sincos then runs on a small argument.
+// Rotate-half RoPE of the pair (lo, hi) = (x_i, x_{i+D/2}) at angle pos*w.
+// The angle (up to ~1e5 rad) is formed and reduced to [-pi, pi] in float64
+// with a two-part 2*pi (Cody-Waite: each fma forms its product exactly and
+// rounds once), so the reduced angle r is good to ~1e-15 rad.  r is then
+// split into float parts rh + rl; sin and cos are taken of the small float
+// argument rh and corrected to first order in rl (|rl| <= 2^-24 pi, so the
+// neglected term is below 1e-14), and the rotation is formed with fused
+// multiply-adds in float32.
 __device__ __forceinline__ void rope_pair(double pos, double w, float lo, float hi, float* out_lo,
                                           float* out_hi) {
   constexpr double kTwoPiHi = 6.283185307179586;             // 2*pi rounded to double
@@ -35,10 +38,14 @@ __device__ __forceinline__ void rope_pair(double pos, double w, float lo, float 
   const double a = pos * w;
   const double k = rint(a * kInvTwoPi);
   const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
-  double sn, cs;
-  sincos(r, &sn, &cs);
-  *out_lo = static_cast<float>(static_cast<double>(lo) * cs - static_cast<double>(hi) * sn);
-  *out_hi = static_cast<float>(static_cast<double>(hi) * cs + static_cast<double>(lo) * sn);
+  const float rh = static_cast<float>(r);
+  const float rl = static_cast<float>(r - static_cast<double>(rh));
+  float s0, c0;
+  sincosf(rh, &s0, &c0);
+  const float sn = fmaf(c0, rl, s0);
+  const float cs = fmaf(-s0, rl, c0);
+  *out_lo = fmaf(lo, cs, -(hi * sn));
+  *out_hi = fmaf(hi, cs, lo * sn);
 }
 
 // Shared-memory scratch of one cache-entry computation.
@@ -57,8 +64,8 @@ struct CompressSmem {
 //   pooling: each (channel pair, token group) thread reduces a strided set
 //   of tokens, then threads < D fold the groups in a fixed order;
 //   GEMV: wave w of the 256 handles rows w, w+4, ...; lanes split the 3d
-//   columns and reduce by butterflies;
-//   RoPE at position j*b in float64, bf16 store (round to nearest even).
+//   columns and reduce across the wave;
+//   RoPE at position j*b (float64 angle), bf16 store (round to nearest even).
 template <int D, int DG>
 __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* row 0 of block */,
                                int64_t st, int BS, const uint16_t* w_k_h, const RopeFreqs& freqs,
@@ -106,8 +113,7 @@ __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* 
         acc = fmaf(bf_lo(wv), sm.u[2 * q2], acc);
         acc = fmaf(bf_hi(wv), sm.u[2 * q2 + 1], acc);
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+      acc = wave_sum(acc);
       if (lane == 0) sm.v[r] = acc;
     }
   }
@@ -122,7 +128,7 @@ __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* 
 
 // Dot product of a gate query (8 float values per lane, lanes of a row
 // group of DG/8 lanes) with one bf16 cache row piece, reduced over the row
-// group by butterflies; every lane of the group ends with the sum.
+// group; every lane of the group ends with the sum.
 template <int DG>
 __device__ __forceinline__ float logit_dot(const float (&qv)[8], uint4 u) {
   constexpr int LPR = DG / 8;
@@ -134,9 +140,7 @@ __device__ __forceinline__ float logit_dot(const float (&qv)[8], uint4 u) {
   s = fmaf(bf_hi(u.z), qv[5], s);
   s = fmaf(bf_lo(u.w), qv[6], s);
   s = fmaf(bf_hi(u.w), qv[7], s);
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  return s;
+  return group_sum<LPR>(s);
 }
 
 }  // namespace seer

@@ -51,6 +51,102 @@ __device__ __forceinline__ uint32_t float_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- cross-lane steps through DPP (a VALU operand modifier, no LDS round
+// trip as with ds_bpermute).  GFX9 dpp_ctrl encodings.
+enum : int {
+  kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+  kDppRowShr = 0x110,       // + n: lane i reads lane i-n of its 16-lane row
+  kDppRowMirror = 0x140,    // lane i reads lane 15-i of its row
+  kDppHalfMirror = 0x141,   // lane i reads lane 7-i of its 8-lane half row
+  kDppRowBcast15 = 0x142,   // lane 15 of the previous row
+  kDppRowBcast31 = 0x143,   // lane 31
+};
+
+// Lane value moved by DPP control CTRL; lanes masked off or whose source
+// lies outside the row read `fill`.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ int dpp_i32(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v), 0));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(dpp_i32<CTRL>(static_cast<int>(v), 0));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group
+// receives the same value (each step adds two equal-ordered partial sums).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  if (N == 16) v += dpp_f32<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the 64 lanes of a wave, the same value in every lane: 16-lane
+// row sums, then the four rows in order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return ((lane_f32(v, 0) + lane_f32(v, 16)) + lane_f32(v, 32)) + lane_f32(v, 48);
+}
+
+// Maximum / minimum over a wave (exact, so the order does not matter).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_f32<kDppXor1>(v));
+  v = fminf(v, dpp_f32<kDppXor2>(v));
+  v = fminf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fminf(v, dpp_f32<kDppRowMirror>(v));
+  return fminf(fminf(lane_f32(v, 0), lane_f32(v, 16)), fminf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppRowMirror>(v));
+  return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = min(v, dpp_u32<kDppXor1>(v));
+  v = min(v, dpp_u32<kDppXor2>(v));
+  v = min(v, dpp_u32<kDppHalfMirror>(v));
+  v = min(v, dpp_u32<kDppRowMirror>(v));
+  return min(min(lane_u32(v, 0), lane_u32(v, 16)), min(lane_u32(v, 32), lane_u32(v, 48)));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within
+// each row, then row 0's total into row 1 (and row 2's into row 3), then
+// the first two rows' total into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp_i32<kDppRowShr + 1>(v, 0);
+  v += dpp_i32<kDppRowShr + 2>(v, 0);
+  v += dpp_i32<kDppRowShr + 4>(v, 0);
+  v += dpp_i32<kDppRowShr + 8>(v, 0);
+  v += dpp_i32<kDppRowBcast15, 0xa>(v, 0);
+  v += dpp_i32<kDppRowBcast31, 0xc>(v, 0);
+  return v;
+}
+
 // Number of K Compression Cache entries after an update that may append up
 // to max_new blocks: min(floor(L/b), c + max_new), never below the clamped
 // old count c.

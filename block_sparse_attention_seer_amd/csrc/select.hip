@@ -4,8 +4,8 @@
 // Adaptation for Long Reasoning"): token-budget top-k on un-softmaxed logits
 // or threshold on the softmax; the incomplete last block is always selected.
 // One 512-thread workgroup per (sequence, KV head) loads the row of logits
-// into LDS; its first wave runs the selection shared with the fused gate
-// kernel, so the staged and the fused paths select identically.
+// into LDS and runs the selection shared with the fused gate kernel (same
+// workgroup size), so the staged and the fused paths select identically.
 #include <cmath>
 
 #include "select_dev.hpp"
@@ -29,7 +29,7 @@ struct SelectParams {
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   extern __shared__ uint32_t s_keys[];  // NBmax floats (bits)
-  __shared__ int s_hist[256];
+  __shared__ SelectSmem s_sel;
   const int pair = blockIdx.x;
   const int b = pair / p.Hkv;
   int L = p.seq_lens[b];
@@ -39,10 +39,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   nc = min(min(max(nc, 0), p.NBmax), L / p.BS);
   const float* z = p.logits + static_cast<int64_t>(pair) * p.NBmax;
   for (int j = threadIdx.x; j < nc; j += kSelThreads) s_keys[j] = __float_as_uint(z[j]);
+  if (threadIdx.x < 256) s_sel.hist[threadIdx.x] = 0;
   __syncthreads();
-  if (threadIdx.x >= 64) return;
-  select_blocks_wave(s_keys, s_hist, nc, total_blocks, p.mode, p.topk, p.log_tau, p.max_sel,
-                     p.block_idx + static_cast<int64_t>(pair) * p.max_sel, p.num_selected + pair);
+  select_blocks_wg<kSelThreads>(s_keys, s_sel, nc, total_blocks, p.mode, p.topk, p.log_tau,
+                                p.max_sel, p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
+                                p.num_selected + pair);
 }
 
 }  // namespace

@@ -8,15 +8,21 @@
 // multiple of b the incomplete last block is always selected.
 // [CP Knowl 6]: the index tensor is [batch, heads_kv, max_selected_blocks].
 //
-// One wave does the whole selection of a (sequence, KV head), so it needs
-// no workgroup barrier: LDS operations of one wave complete in issue order,
-// and cross-lane steps are shuffles.  Top-k is an exact radix select over
-// order-preserving 32-bit keys, most significant 8 bits first: each pass
-// histograms the keys still in play and keeps the bucket holding the k-th
-// largest key; it stops as soon as that bucket is taken whole, and only
-// exact duplicates of the k-th key need all four passes and a rank so that
-// the lower indices win.  Output order is ascending block index via a wave
-// prefix sum over contiguous per-lane index ranges -- no sort is needed.
+// The whole workgroup selects; thread t owns a contiguous range of block
+// indices, so a workgroup prefix sum over per-thread counts writes the
+// selected indices in ascending order without a sort.
+//
+// Top-k is an exact selection by narrowing: the keys still "in play" always
+// form one interval [lo, hi] of the order-preserving 32-bit key (every key
+// above hi is taken, every key below lo is not), and `need` of them are
+// still to take.  Each pass histograms the in-play keys into 256 buckets,
+// keeps the bucket that holds the need-th largest and stops once that bucket
+// is to be taken whole.  The first pass buckets linearly on the float value
+// between the smallest and largest logit, which for logits of similar size
+// leaves a handful of keys in play; later passes bucket on the key bits
+// below the interval's leading bit (8 bits per pass, so at most four).  If
+// the interval closes on one value, its duplicates are taken in index order
+// (lower index first).
 #pragma once
 
 #include "../../include/seer.h"
@@ -24,146 +30,264 @@
 
 namespace seer {
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
+constexpr int kSelMaxWaves = 16;
+
+struct SelectSmem {
+  int hist[256];
+  float fred[2][kSelMaxWaves];
+  uint32_t ured[2][kSelMaxWaves];
+  int scan[2][kSelMaxWaves];
+  int pick[3];
+};
+
+// Exclusive prefix sum of v over the workgroup in thread order, and the
+// total.  `part` (NT/64 ints of LDS) must not be in use by another scan
+// that some thread may still be reading.
+template <int NT>
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* part, int* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int incl = wave_inclusive_scan(v);
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
+  for (int i = 0; i < NW; ++i) {
+    const int s = part[i];
+    before += (i < w) ? s : 0;
+    tot += s;
   }
-  return v;
+  *total = tot;
+  return before + incl - v;
 }
 
-// Orders LDS traffic of this wave: every earlier LDS access has completed.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+template <int NT>
+__device__ __forceinline__ void wg_minmax_f(float& mn, float& mx, SelectSmem& sm) {
+  constexpr int NW = NT / 64;
+  const int w = threadIdx.x >> 6;
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) {
+    sm.fred[0][w] = mn;
+    sm.fred[1][w] = mx;
+  }
+  __syncthreads();
+  mn = sm.fred[0][0];
+  mx = sm.fred[1][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    mn = fminf(mn, sm.fred[0][i]);
+    mx = fmaxf(mx, sm.fred[1][i]);
+  }
 }
 
-// Called by the 64 lanes of one wave.  keys[0..nc) (LDS) hold the logits of
-// the scored blocks as float bits and are overwritten; hist is 256 ints of
-// LDS.  Appends the unscored blocks nc .. total_blocks-1 and writes the
-// ascending, -1 padded row out[0..max_sel) plus its count.
-__device__ void select_blocks_wave(uint32_t* keys, int* hist, int nc, int total_blocks, int mode,
-                                   int topk, float log_tau, int max_sel, int32_t* out,
-                                   int32_t* count_out) {
-  const int lane = threadIdx.x & 63;
-  const int vpl = (nc + 63) / 64;
-  const int j0 = min(nc, lane * vpl);
-  const int j1 = min(nc, j0 + vpl);
+template <int NT>
+__device__ __forceinline__ void wg_minmax_u(uint32_t& mn, uint32_t& mx, SelectSmem& sm) {
+  constexpr int NW = NT / 64;
+  const int w = threadIdx.x >> 6;
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if ((threadIdx.x & 63) == 0) {
+    sm.ured[0][w] = mn;
+    sm.ured[1][w] = mx;
+  }
+  __syncthreads();
+  mn = sm.ured[0][0];
+  mx = sm.ured[1][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    mn = min(mn, sm.ured[0][i]);
+    mx = max(mx, sm.ured[1][i]);
+  }
+}
 
-  // Top-k: a key is taken iff (key & pmask) > prefix, or it equals prefix
-  // and it is within the first `need` such keys by index (or all of them
-  // when the bucket holds exactly `need`).
-  bool take_all = false, take_none = false, exact = true;
-  uint32_t prefix = 0, pmask = 0;
+// After the histogram of this pass is complete (sm.hist, callers add to it
+// before calling): the bucket holding the need-th largest counted key, the
+// number of counted keys in higher buckets, and that bucket's count.  Wave 0
+// scans and clears the histogram for the next pass.  1 <= need <= counted.
+template <int NT>
+__device__ __forceinline__ void hist_pick(SelectSmem& sm, int need, int& bucket, int& above,
+                                          int& count) {
+  __syncthreads();
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    int hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[i] = sm.hist[4 * lane + i];
+      sm.hist[4 * lane + i] = 0;
+    }
+    const int mine = (hb[0] + hb[1]) + (hb[2] + hb[3]);
+    const int incl = wave_inclusive_scan(mine);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int suf = total - incl + mine;  // keys in buckets >= 4*lane
+    int cnt = suf - mine;                 // keys in buckets >= 4*lane + 4
+    if (cnt < need && need <= suf) {      // exactly one lane
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (cnt + hb[i] >= need) {
+          sm.pick[0] = 4 * lane + i;
+          sm.pick[1] = cnt;
+          sm.pick[2] = hb[i];
+          break;
+        }
+        cnt += hb[i];
+      }
+    }
+  }
+  __syncthreads();
+  bucket = sm.pick[0];
+  above = sm.pick[1];
+  count = sm.pick[2];
+}
+
+// Called by all NT threads of the workgroup once keys[0..nc) (LDS, the
+// logits as float bits) are visible to every thread.  sm.hist must be zero
+// on entry and is left zero.  Appends the unscored blocks nc ..
+// total_blocks-1 and writes the ascending, -1 padded row out[0..max_sel)
+// plus its count.
+template <int NT>
+__device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSmem& sm, int nc,
+                                                 int total_blocks, int mode, int topk,
+                                                 float log_tau, int max_sel, int32_t* out,
+                                                 int32_t* count_out) {
+  static_assert(NT % 64 == 0 && NT / 64 <= kSelMaxWaves, "workgroup size");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int vpt = (nc + NT - 1) / NT;
+  const int j0 = min(nc, tid * vpt);
+  const int j1 = min(nc, j0 + vpt);
+
+  // A key is taken iff  key > lo, or key == lo and (whole || rank < need)
+  // (top-k), or z > thr (threshold); `all` / `none` short-cut both.
+  bool all = false, none = false, whole = true;
+  uint32_t lo = 0;
   int need = 0;
-  float thr = 0.f;  // threshold mode: logit bound
+  float thr = 0.f;
 
   if (mode == SEER_SELECT_TOPK) {
     const int k = min(topk, nc);
     if (k >= nc) {
-      take_all = true;
+      all = true;
     } else if (k <= 0) {
-      take_none = true;
+      none = true;
     } else {
-      for (int j = j0; j < j1; ++j) keys[j] = float_key(__uint_as_float(keys[j]));
       need = k;
-      exact = false;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
-        wave_lds_sync();
+      int m = nc;  // keys in play
+      float zmn = INFINITY, zmx = -INFINITY;
+      for (int j = j0; j < j1; ++j) {
+        const float z = __uint_as_float(keys[j]);
+        zmn = fminf(zmn, z);
+        zmx = fmaxf(zmx, z);
+      }
+      wg_minmax_f<NT>(zmn, zmx, sm);
+      const float scale = 256.f / (zmx - zmn);
+      uint32_t hi;
+      if (zmx > zmn && scale > 0.f && scale < INFINITY) {
+        // linear buckets on the value; monotone in z (NaN counts lowest)
+        auto fbucket = [&](float z) -> int {
+          return (z == z) ? min(255, static_cast<int>((z - zmn) * scale)) : 0;
+        };
+        for (int j = j0; j < j1; ++j) atomicAdd(&sm.hist[fbucket(__uint_as_float(keys[j]))], 1);
+        int b, above;
+        hist_pick<NT>(sm, need, b, above, m);
+        need -= above;
+        // the kept bucket as an interval of keys
+        uint32_t kmn = 0xffffffffu, kmx = 0u;
         for (int j = j0; j < j1; ++j) {
-          const uint32_t key = keys[j];
-          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-        }
-        wave_lds_sync();
-        // lane covers digits 4*lane .. 4*lane+3; suffix sums from the top
-        int hb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hb[i] = hist[4 * lane + i];
-        const int mine = hb[0] + hb[1] + hb[2] + hb[3];
-        int suf = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_down(suf, o);
-          if (lane + o < 64) suf += t;
-        }
-        const int above_group = suf - mine;  // keys with a digit above this lane's
-        const bool owner = above_group < need && need <= suf;
-        int cnt = above_group, dsel = 4 * lane, bucket = hb[0];
-        if (owner) {
-          for (int i = 3; i >= 0; --i) {
-            if (cnt + hb[i] >= need) {
-              dsel = 4 * lane + i;
-              bucket = hb[i];
-              break;
-            }
-            cnt += hb[i];
+          const float z = __uint_as_float(keys[j]);
+          if (fbucket(z) == b) {
+            const uint32_t key = float_key(z);
+            kmn = min(kmn, key);
+            kmx = max(kmx, key);
           }
         }
-        const unsigned long long m = __ballot(owner);
-        const int src = __ffsll(static_cast<long long>(m)) - 1;  // exactly one owner lane
-        dsel = __shfl(dsel, src);
-        cnt = __shfl(cnt, src);
-        bucket = __shfl(bucket, src);
-        prefix |= static_cast<uint32_t>(dsel) << shift;
-        pmask |= 0xffu << shift;
-        need -= cnt;
-        wave_lds_sync();  // every lane has read the histogram
-        if (bucket == need) {  // the k-th key's bucket is taken whole
-          exact = true;
-          break;
+        wg_minmax_u<NT>(kmn, kmx, sm);
+        lo = kmn;
+        hi = kmx;
+      } else {
+        uint32_t kmn = 0xffffffffu, kmx = 0u;
+        for (int j = j0; j < j1; ++j) {
+          const uint32_t key = float_key(__uint_as_float(keys[j]));
+          kmn = min(kmn, key);
+          kmx = max(kmx, key);
         }
+        wg_minmax_u<NT>(kmn, kmx, sm);
+        lo = kmn;
+        hi = kmx;
       }
+      // narrow on key bits until the kept bucket is taken whole or is a
+      // single value
+      while (m != need && lo != hi) {
+        const int shift = max(0, 32 - __clz(static_cast<int>(hi - lo)) - 8);
+        for (int j = j0; j < j1; ++j) {
+          const uint32_t key = float_key(__uint_as_float(keys[j]));
+          if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> shift], 1);
+        }
+        int b, above;
+        hist_pick<NT>(sm, need, b, above, m);
+        need -= above;
+        const uint64_t nlo = static_cast<uint64_t>(lo) + (static_cast<uint64_t>(b) << shift);
+        const uint64_t nhi = nlo + (uint64_t{1} << shift) - 1;
+        lo = static_cast<uint32_t>(nlo);
+        hi = static_cast<uint32_t>(min(nhi, static_cast<uint64_t>(hi)));
+      }
+      whole = (m == need);
     }
   } else {
-    // softmax_j > tau  <=>  z_j > ln(tau) + logsumexp(z)
+    // softmax_j > tau  <=>  z_j > ln(tau) + logsumexp(z); fixed summation order
     float mx = -INFINITY;
     for (int j = j0; j < j1; ++j) mx = fmaxf(mx, __uint_as_float(keys[j]));
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) sm.fred[0][tid >> 6] = mx;
+    __syncthreads();
+    mx = sm.fred[0][0];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int i = 1; i < NW; ++i) mx = fmaxf(mx, sm.fred[0][i]);
     float se = 0.f;
     if (nc > 0)
       for (int j = j0; j < j1; ++j) se += expf(__uint_as_float(keys[j]) - mx);
+    se = wave_sum(se);
+    if ((tid & 63) == 0) sm.fred[1][tid >> 6] = se;
+    __syncthreads();
+    se = sm.fred[1][0];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) se += __shfl_xor(se, o);
+    for (int i = 1; i < NW; ++i) se += sm.fred[1][i];
     thr = (nc > 0) ? log_tau + (mx + logf(se)) : INFINITY;
   }
 
-  // ranks among keys equal to the final prefix (only for exact ties)
+  const bool topk_range = (mode == SEER_SELECT_TOPK) && !all && !none;
+  // ranks among the duplicates of lo, in index order (only if not whole)
   int eq_before = 0;
-  if (mode == SEER_SELECT_TOPK && !take_all && !take_none && !exact) {
+  if (topk_range && !whole) {
     int eq = 0;
-    for (int j = j0; j < j1; ++j) eq += ((keys[j] & pmask) == prefix);
-    eq_before = wave_inclusive_scan(eq) - eq;
+    for (int j = j0; j < j1; ++j) eq += (float_key(__uint_as_float(keys[j])) == lo);
+    int unused;
+    eq_before = wg_exclusive_scan<NT>(eq, sm.scan[0], &unused);
   }
-  auto selected = [&](int j, int& rank) -> bool {
+  auto taken = [&](int j, int& rank) -> bool {
     if (mode != SEER_SELECT_TOPK) return __uint_as_float(keys[j]) > thr;
-    if (take_all) return true;
-    if (take_none) return false;
-    const uint32_t mk = keys[j] & pmask;
-    if (mk > prefix) return true;
-    if (mk < prefix) return false;
-    const bool take = exact || rank < need;
+    if (all) return true;
+    if (none) return false;
+    const uint32_t key = float_key(__uint_as_float(keys[j]));
+    if (key > lo) return true;
+    if (key < lo) return false;
+    const bool t = whole || rank < need;
     ++rank;
-    return take;
+    return t;
   };
   int nsel = 0;
   {
     int rank = eq_before;
-    for (int j = j0; j < j1; ++j) nsel += selected(j, rank);
+    for (int j = j0; j < j1; ++j) nsel += taken(j, rank);
   }
-  const int incl = wave_inclusive_scan(nsel);
-  const int scored_total = __shfl(incl, 63);
+  int scored_total;
+  int pos = wg_exclusive_scan<NT>(nsel, sm.scan[1], &scored_total);
   {
     int rank = eq_before;
-    int pos = incl - nsel;
     for (int j = j0; j < j1; ++j) {
-      if (selected(j, rank)) {
+      if (taken(j, rank)) {
         if (pos < max_sel) out[pos] = j;
         ++pos;
       }
@@ -171,13 +295,13 @@ __device__ void select_blocks_wave(uint32_t* keys, int* hist, int nc, int total_
   }
   // blocks without a cache entry (normally the partial block) are forced
   const int forced = max(0, total_blocks - nc);
-  for (int f = lane; f < forced; f += 64) {
-    const int pos = scored_total + f;
-    if (pos < max_sel) out[pos] = nc + f;
+  for (int f = tid; f < forced; f += NT) {
+    const int p = scored_total + f;
+    if (p < max_sel) out[p] = nc + f;
   }
   const int written = min(scored_total + forced, max_sel);
-  for (int i = written + lane; i < max_sel; i += 64) out[i] = -1;
-  if (lane == 0) *count_out = written;
+  for (int i = written + tid; i < max_sel; i += NT) out[i] = -1;
+  if (tid == 0) *count_out = written;
 }
 
 }  // namespace seer

@@ -333,6 +333,8 @@ def test_select_topk_exact(S, nbm, bs, k, quant):
         z = (np.round(z / quant) * quant).astype(np.float32)
     z[1, 0, 5] = -np.inf
     z[1, 1, :] = 0.0
+    z[0, 1, 7] = 1e30  # one far outlier: the rest share a few value buckets
+    z[0, 2, :] = 2.0 ** -(np.arange(nbm) % 140)  # geometric, with exact repeats
     seq = [lmax, lmax - 5, 3 * bs + 1, bs - 1, 2 * bs]
     kl = [lmax // bs, (lmax - 5) // bs, 1, 0, 2]  # sequence 2: cache lags by two blocks
     max_sel = min(k + 3, nbm)
@@ -507,20 +509,26 @@ def test_fused_step_equals_staged(S, name, overrides):
     mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
     a = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
     b = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
+    c = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
     seq = inp["seq_lens"]
     a.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
     _clone_state(a, b)
+    _clone_state(a, c)
+    c.logits.fill_(123.0)
     args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
     a.step(*args)
     b.fused_step(*args)
+    c.fused_step(*args, keep_logits=False)  # logits pointer NULL
     torch.cuda.synchronize()
-    assert torch.equal(a.kcomp_lens, b.kcomp_lens)
-    assert torch.equal(a.kcomp, b.kcomp)
-    assert torch.equal(a.num_selected, b.num_selected)
-    assert torch.equal(a.block_idx, b.block_idx)
-    assert torch.equal(a.out, b.out)
-    assert torch.equal(a.lse, b.lse)
+    for x in (b, c):
+        assert torch.equal(a.kcomp_lens, x.kcomp_lens)
+        assert torch.equal(a.kcomp, x.kcomp)
+        assert torch.equal(a.num_selected, x.num_selected)
+        assert torch.equal(a.block_idx, x.block_idx)
+        assert torch.equal(a.out, x.out)
+        assert torch.equal(a.lse, x.lse)
     assert torch.equal(a.logits, b.logits)
+    assert bool((c.logits == 123.0).all())  # untouched
     # the fused workspace's counters are left at zero
     assert int(b.step_ws[: w.batch * w.num_kv_heads].view(torch.int32).abs().sum()) == 0
     # one pair against the oracle as well
