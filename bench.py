@@ -34,7 +34,8 @@ METRIC = ("sparse decode µs/step + achieved HBM GB/s (% peak); "
           "speedup vs dense @90% sparsity")
 PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_seer_amd", "csrc", "decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "block_sparse_attention_seer_amd", "csrc", f)
+               for f in ("decode.hip", "seer_device.hpp")]
 
 
 def log(msg: str) -> None:
@@ -42,8 +43,13 @@ def log(msg: str) -> None:
 
 
 def decode_src_hash() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the decode kernel's sources (the kernel file and its device
+    helpers): stored counter figures apply only to the kernel they measured."""
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -70,7 +76,13 @@ def main() -> int:
     ap.add_argument("--num-split", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="for rocprofv3 --pmc runs: a few decode launches and a plain copy of "
+                         "known size (the counters' scale), then exit")
     args = ap.parse_args()
+    if args.traffic_pass:
+        args.replicas = min(args.replicas, 2)
+        args.warmup = max(args.warmup, 2)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode path of one layer is measured on a "
@@ -133,6 +145,9 @@ def main() -> int:
         step(i % R)
     torch.cuda.synchronize()
 
+    if args.traffic_pass:
+        return traffic_pass(reps, decode_only, torch, dev, L, bs, d)
+
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -144,31 +159,20 @@ def main() -> int:
 
     # the dominant kernel alone, event-timed on the stream it runs on, on the
     # same replicas and the selections the steps just made
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # (the binding launches on torch's current stream, which these events see)
     log(f"timing {args.steps} decode launches")
-    for i in range(args.steps):
-        evs[i][0].record()
-        decode_only(i % R)
-        evs[i][1].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_us = 1e3 * float(np.mean(dec_ms))
-    dec_us_med = 1e3 * float(np.median(dec_ms))
+    e0.record()
+    for i in range(args.steps):
+        decode_only(i % R)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_us = 1e3 * e0.elapsed_time(e1) / args.steps
 
     # ---- algorithmic bytes (per step, from the actual selections)
-    sel_tokens = []
     nb = L // bs
-    for inp, st in reps:
-        ns = st.num_selected.cpu().numpy()
-        idx = st.block_idx.cpu().numpy()
-        tot = 0
-        for b_ in range(B):
-            for h_ in range(Hkv):
-                for j in idx[b_, h_, :ns[b_, h_]]:
-                    tot += min(bs, L - int(j) * bs)
-        sel_tokens.append(tot)
-    sel_tokens = float(np.mean(sel_tokens))
+    sel_tokens = float(np.mean([selected_tokens(st, L, bs) for _, st in reps]))
     qo_bytes = 2 * B * Hq * d * 2
     kv_bytes = sel_tokens * 2 * d * 2
     idx_bytes = B * Hkv * (reps[0][1].max_selected + 1) * 4
@@ -251,9 +255,9 @@ def main() -> int:
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes": int(decode_alg),
             "avg_launch_us": round(dec_us, 3),
-            "median_launch_us": round(dec_us_med, 3),
-            "timing": "HIP events around each decode launch, same stream, replicas and "
-                      "selections as the timed steps",
+            "timing": "one HIP event pair on the launch stream around K back-to-back decode "
+                      "launches (same replicas and selections as the timed steps); avg = "
+                      "elapsed / K",
         },
         "step_algorithmic_bytes": int(step_alg),
         "step_GBps": round(step_gbps, 1),
@@ -268,6 +272,45 @@ def main() -> int:
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def selected_tokens(st, L, bs):
+    ns = st.num_selected.cpu().numpy()
+    idx = st.block_idx.cpu().numpy()
+    tot = 0
+    for b_ in range(ns.shape[0]):
+        for h_ in range(ns.shape[1]):
+            for j in idx[b_, h_, :ns[b_, h_]]:
+                tot += min(bs, L - int(j) * bs)
+    return tot
+
+
+def traffic_pass(reps, decode_only, torch, dev, L, bs, d):
+    """Ten decode launches over the replicas, then three copies of 256 MiB
+    through torch.neg (reads 256 MiB, writes 256 MiB): under rocprofv3 --pmc
+    the copy's FETCH_SIZE / WRITE_SIZE give the counters' scale."""
+    n = 10
+    for i in range(n):
+        decode_only(i % len(reps))
+    torch.cuda.synchronize()
+    copy_bytes = 256 << 20
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    per_rep = []
+    for inp, st in reps:
+        B, Hq = inp["q"].shape[0], inp["q"].shape[1]
+        idx_bytes = st.block_idx.numel() * 4 + st.num_selected.numel() * 4
+        per_rep.append(selected_tokens(st, L, bs) * 2 * d * 2 + 2 * B * Hq * d * 2 + idx_bytes)
+    alg = sum(per_rep[i % len(reps)] for i in range(n)) / n
+    print(json.dumps({"traffic_pass": True, "decode_launches": n,
+                      "decode_algorithmic_bytes_per_launch": int(alg),
+                      "copy_kernel": "neg_kernel", "copy_read_bytes": copy_bytes,
+                      "copy_write_bytes": copy_bytes, "copies": 3,
+                      "decode_src_sha256_16": decode_src_hash()}), flush=True)
     return 0
 
 

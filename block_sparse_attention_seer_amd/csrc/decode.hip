@@ -11,9 +11,10 @@
 //
 // MI355X design (not the pages' H100 design):
 //   * one workgroup = NW waves = one split of one (b, h).  The (b, h)'s
-//     active tokens form 16-token tiles; every wave of its S splits takes an
-//     even contiguous range of tiles (so the work is balanced to one tile)
-//     and walks it 64 tokens at a time with its own online softmax;
+//     active blocks are cut into 64-token chunks; split s owns the s-th of S
+//     even chunk ranges and deals them round-robin to its waves, each
+//     keeping its own online softmax.  The index row is staged in LDS,
+//     requested together with the selection count;
 //   * both contractions run on MFMA v_mfma_f32_16x16x32_bf16 with the g
 //     query heads of the group padded to 16:
 //       S^T[token][head] = K[token][:] . q[head][:]      (A = K rows straight
@@ -23,19 +24,25 @@
 //     The score accumulators already sit in the P operand's layout, so P
 //     never leaves registers.  V is loaded as 8-byte pieces (4 dims of one
 //     token) and the B operand (8 tokens of one dim) is assembled with
-//     byte permutes, so V never goes through LDS;
+//     byte permutes, so V never goes through LDS.  All K and V loads of a
+//     chunk (32 KiB per wave at d = 128) are in flight together;
 //   * the waves of a split merge in LDS; with one split the workgroup writes
-//     the output directly, otherwise it writes an (lse, o) partial and a
-//     second small kernel merges the splits.  (Merging inside the launch
-//     would need device-scope release/acquire, which on gfx950 turns into
-//     L2 write-back / invalidate operations that serialise across
-//     workgroups -- measured far slower than a second launch.)
+//     the output directly.  Otherwise each split writes an (lse, o) partial
+//     with device-coherent stores, counts itself on a per-(b, h) counter,
+//     and the split that completes the count merges all partials (coherent
+//     loads), writes the output and resets the counter.  Coherent accesses
+//     go around the per-XCD L2, so no release/acquire fence is needed: those
+//     turn into L2 write-back / invalidate on gfx950, which serialise across
+//     workgroups.  Without counters in the workspace a second small kernel
+//     merges the splits instead.
 #include "seer_device.hpp"
 #include "seer_internal.h"
 
 namespace seer {
 
 namespace {
+
+constexpr int kIdxLds = 512;  // index-row entries staged in LDS per workgroup
 
 struct DecodeParams {
   const uint16_t* q;
@@ -94,6 +101,13 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
                                           p.commit_max_new);
   }
 
+  const int32_t* idx = DENSE ? nullptr : p.block_idx + static_cast<int64_t>(pair) * p.max_sel;
+  // The first kIdxLds entries of the index row go to LDS, requested at once
+  // with the selection count instead of after it.
+  __shared__ int s_idx[kIdxLds];
+  if (!DENSE)
+    for (int i = tid; i < min(p.max_sel, kIdxLds); i += NW * 64) s_idx[i] = idx[i];
+
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.Lmax);
   const int nblk = (L + BS - 1) / BS;
@@ -104,19 +118,18 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     nslots = p.num_selected[pair];
     nslots = min(max(nslots, 0), p.max_sel);
   }
-  // The pair's active tokens, block after block, form 16-token tiles
-  // (a block holds BS/16 of them); the S*NW waves of the pair each take an
-  // even, contiguous range of tiles and walk it four tiles at a time.
-  constexpr int TPB = BS / 16;
-  const int T = nslots * TPB;
-  const int GW = S * NW;
-  const int gw = split * NW + w;
-  const int ta = static_cast<int>(static_cast<int64_t>(T) * gw / GW);
-  const int tb = static_cast<int>(static_cast<int64_t>(T) * (gw + 1) / GW);
+  // Work unit: a 64-token chunk (four 16-token tiles) of an active block.
+  // The pair's chunks are cut into S even ranges, one per split; wave w of a
+  // split takes chunks c_begin + w, c_begin + w + NW, ...  (A fixed
+  // assignment keeps the summation order, and so the output bits, the same
+  // from run to run.)
+  constexpr int CPB = BS / 64;
+  const int nchunks = nslots * CPB;
+  const int c_begin = static_cast<int>(static_cast<int64_t>(nchunks) * split / S);
+  const int c_end = static_cast<int>(static_cast<int64_t>(nchunks) * (split + 1) / S);
 
   const uint16_t* kb = p.k + b * p.sb + h * p.sh;
   const uint16_t* vb = p.v + b * p.sb + h * p.sh;
-  const int32_t* idx = DENSE ? nullptr : p.block_idx + static_cast<int64_t>(pair) * p.max_sel;
 
   // q of head ln as the B operand of the score MFMA (zero for padding heads).
   uint4 qop[KS];
@@ -133,28 +146,17 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int t = 0; t < VH * 4; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int last = L - 1;
+  __syncthreads();
 
-  for (int t = ta; t < tb; t += 4) {
-    // first token of each of the four tiles, or -1 (outside the range, an
-    // invalid index entry, or past the sequence)
+  for (int c = c_begin + w; c < c_end; c += NW) {
+    const int slot = c / CPB;
+    const int blk = DENSE ? slot : (slot < kIdxLds ? s_idx[slot] : idx[slot]);
+    const int base = blk * BS + (c - slot * CPB) * 64;
+    if (blk < 0 || blk >= nblk || base >= L) continue;  // invalid entry: skipped
+    // first token of each of the four tiles, or -1 past the sequence
     int tok0[4];
-    bool any = false;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      int base = -1;
-      const int u = t + nt;
-      if (u < tb) {
-        const int slot = u / TPB;
-        const int blk = DENSE ? slot : idx[slot];
-        if (blk >= 0 && blk < nblk) {
-          const int t0 = blk * BS + (u - slot * TPB) * 16;
-          if (t0 < L) base = t0;
-        }
-      }
-      tok0[nt] = base;
-      any = any || base >= 0;
-    }
-    if (!any) continue;
+    for (int nt = 0; nt < 4; ++nt) tok0[nt] = (base + 16 * nt < L) ? base + 16 * nt : -1;
 
     // K rows tok0 + ln, dims 32*s + 8*lq .. +7 (the A operand).
     uint4 kr[4][KS];
@@ -507,9 +509,10 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dense = (a.block_idx == nullptr);
   const int key = (d.head_dim == 128 ? 4 : 0) | (d.block_size == 128 ? 2 : 0) | (dense ? 1 : 0);
-  const int nw = (a.waves_per_group == 4 || (a.waves_per_group == 8 && G <= 8))
-                     ? a.waves_per_group
-                     : decode_waves_per_group(pairs, S, G);
+  const int wpg = a.waves_per_group;
+  const int nw = ((wpg == 4 || wpg == 8) && decode_waves_fit(wpg, G, d.head_dim))
+                     ? wpg
+                     : decode_waves_per_group(G, d.head_dim);
   if (nw == 8)
     launch_variant<8>(key, p, grid, s);
   else

@@ -109,30 +109,34 @@ size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim)
 }
 
 int auto_num_split(const seer_dims* d, int max_blocks, int num_cus) {
-  // Measured on MI355X: the decode kernel saturates HBM with about eight
-  // waves per compute unit, and one compute unit alone sustains only about
-  // 28 GB/s, so every CU needs work.  Aim at 8 waves per CU in total, using
-  // the workgroup size the launcher picks, but give each workgroup at least
-  // one 64-token chunk.
+  // Measured on MI355X: the decode kernel keeps HBM busy once about eight
+  // waves per compute unit are in flight chip-wide (each wave streams its
+  // chunks with all loads of a chunk outstanding), so every CU needs work:
+  // aim at 8 waves per CU in total with the workgroup size the launcher
+  // picks, but no more splits than leave one 64-token chunk per wave (more
+  // would only add partials to merge, not bytes in flight).
   const int g = d->num_q_heads / d->num_kv_heads;
   const int64_t pairs = static_cast<int64_t>(d->batch) * d->num_kv_heads;
   const int64_t chunks = static_cast<int64_t>(max_blocks) * (d->block_size / 64);
   const int cus = num_cus > 0 ? num_cus : 256;
-  const int nw = decode_waves_per_group(pairs, 1, g);
+  const int nw = decode_waves_per_group(g, d->head_dim);
   const int64_t target_wgs = static_cast<int64_t>(cus) * 8 / nw;
   int64_t s = (target_wgs + pairs - 1) / pairs;
-  if (s > chunks) s = chunks;
+  if (s > chunks / nw) s = chunks / nw;
   if (s < 1) s = 1;
   if (s > kMaxSplit) s = kMaxSplit;
   return static_cast<int>(s);
 }
 
-int decode_waves_per_group(int64_t pairs, int num_split, int g) {
-  // Eight waves per workgroup whenever the wave merge fits 32 KiB of LDS
-  // (g <= 8), four otherwise.
-  (void)pairs;
-  (void)num_split;
-  return g <= 8 ? 8 : 4;
+bool decode_waves_fit(int nw, int g, int head_dim) {
+  return static_cast<int64_t>(nw) * g * head_dim * static_cast<int64_t>(sizeof(float)) <=
+         kDecodeMergeLds;
+}
+
+int decode_waves_per_group(int g, int head_dim) {
+  // Eight waves (one workgroup per CU at the kernel's register use) when
+  // their merge (8 x g x head_dim floats of LDS) fits the budget, else four.
+  return decode_waves_fit(8, g, head_dim) ? 8 : 4;
 }
 
 }  // namespace seer

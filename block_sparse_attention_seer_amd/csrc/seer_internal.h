@@ -14,6 +14,7 @@ namespace seer {
 constexpr int kMaxGroup = 16;          // query heads per KV head (MFMA N = 16)
 constexpr int kMaxNBSelect = 8192;     // blocks per sequence the select kernel holds in LDS
 constexpr int kMaxSplit = 128;         // splits per (b, h) in the decode kernel
+constexpr int kDecodeMergeLds = 48 * 1024;  // LDS bytes for the decode wave merge
 constexpr int kCounterBytes = 256;     // alignment of the partial outputs after the partial lse
 
 // ------------------------------------------------------- argument checks
@@ -97,7 +98,7 @@ struct DecodeArgs {
   int max_selected;             // index row length (sparse)
   float scale;
   int num_split;
-  int waves_per_group;          // 0 = automatic (4 or 8)
+  int waves_per_group;          // 0 = automatic (8 or 4)
   bool merge_inline;            // merge splits in the decode launch (counters in the workspace)
   void* workspace;
   uint16_t* out;
@@ -108,7 +109,10 @@ struct DecodeArgs {
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
 
 // Waves per decode workgroup chosen automatically.
-int decode_waves_per_group(int64_t pairs, int num_split, int g);
+// Waves per decode workgroup (8 or 4) and whether nw waves fit the LDS
+// budget of the wave merge.
+int decode_waves_per_group(int g, int head_dim);
+bool decode_waves_fit(int nw, int g, int head_dim);
 
 // Device query (HIP): compute units of the current device, cached.
 int device_cu_count(int* out);

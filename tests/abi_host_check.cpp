@@ -76,17 +76,21 @@ int main() {
   const size_t ws = seer::decode_workspace_bytes(128, 4, 5, 128);
   EXPECT(ws == 512 + 10240 + 128u * 4 * 5 * 128 * 4);
   EXPECT(seer::decode_workspace_bytes(3, 2, 1, 64) == 256 + 256 + 3u * 2 * 64 * 4);
-  // automatic split: about 8 waves per compute unit in total (8-wave
-  // workgroups for g <= 8), at most one split per 64-token chunk
-  EXPECT(seer::decode_waves_per_group(128, 2, 5) == 8);
-  EXPECT(seer::decode_waves_per_group(128, 2, 16) == 4);
-  EXPECT(seer::auto_num_split(&d, 53, 256) == 2);     // 128 pairs x 2 x 8 waves
+  // automatic split: 8-wave workgroups when their wave merge fits 48 KiB of
+  // LDS (else 4), about 8 waves per compute unit in total, no more splits
+  // than leave a 64-token chunk per wave
+  EXPECT(seer::decode_waves_per_group(5, 128) == 8);
+  EXPECT(seer::decode_waves_per_group(12, 128) == 8);  // 48 KiB
+  EXPECT(seer::decode_waves_per_group(13, 128) == 4);
+  EXPECT(seer::decode_waves_per_group(16, 64) == 8);
+  EXPECT(!seer::decode_waves_fit(8, 13, 128) && seer::decode_waves_fit(4, 13, 128));
+  EXPECT(seer::auto_num_split(&d, 53, 256) == 2);      // 128 pairs x 2 x 8 waves
   seer_dims one = good();
   one.batch = 1;
-  EXPECT(seer::auto_num_split(&one, 65, 256) == 32);  // 8 pairs fill 256 CUs
-  EXPECT(seer::auto_num_split(&one, 3, 256) == 3);    // never more splits than chunks
+  EXPECT(seer::auto_num_split(&one, 65, 256) == 8);    // 65 chunks: 8 per split
+  EXPECT(seer::auto_num_split(&one, 3, 256) == 1);     // too few chunks to split
   seer_dims wide = good();
-  wide.num_q_heads = 128;                             // g = 16: 4-wave groups
+  wide.num_q_heads = 128;                              // g = 16: 4-wave groups
   EXPECT(seer::auto_num_split(&wide, 53, 256) == 4);
 
   if (failures == 0) std::printf("abi host checks: all passed\n");
