@@ -70,7 +70,8 @@ constexpr int kQueryStepsPerWave = 16;  // k-steps of 32 per wave: g*d <= 2048
 // Gate-query tile t: 16 gate rows (rows i0..i0+7 and their RoPE partners
 // i0+DG/2..) x 16 sequences of one KV head as MFMA D = W_q . X.  The 4 waves
 // split the g*d contraction; each issues all of its loads before its first
-// MFMA; the partial tiles are summed in a fixed order.
+// MFMA; the partial tiles are summed in a fixed order, and wave w rotates
+// and stores element w of every lane's accumulator.
 template <int D, int DG>
 __device__ void query_tile(const PrepParams& p, int t, float (*red)[64][4]) {
   const int RT = DG / 16;
@@ -91,6 +92,8 @@ __device__ void query_tile(const PrepParams& p, int t, float (*red)[64][4]) {
   const int bq = b0 + ln;
   const bool bvalid = bq < p.B;
   int L = bvalid ? p.seq_lens[bq] : 1;  // issued early; used by the rotation
+  // frequency of the row this lane rotates (element w of its tile column), also early
+  const double wf = p.freqs.w[i0 + ((4 * lq + w) & 7)];
 
   const int arow = (ln < 8) ? (i0 + ln) : (half + i0 + ln - 8);
   const uint16_t* wrow = p.w_q + (static_cast<int64_t>(h) * DG + arow) * K + 8 * lq;
@@ -111,26 +114,20 @@ __device__ void query_tile(const PrepParams& p, int t, float (*red)[64][4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[w][lane][r] = acc[r];
   __syncthreads();
-  if (w != 0) return;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    acc[r] = ((red[0][lane][r] + red[1][lane][r]) + red[2][lane][r]) + red[3][lane][r];
-  // acc[r] = Y[tile row 4*lq + r][sequence b0 + ln]
+  // wave w finishes element r = w of every lane: Y[tile row 4*lq + w][sequence b0 + ln]
+  const int r = w;
+  const float mine = ((red[0][lane][r] + red[1][lane][r]) + red[2][lane][r]) + red[3][lane][r];
   L = min(max(L, 0), p.Lmax);
   const double pos = static_cast<double>(L - 1);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float mine = acc[r];
-    const float other = __shfl_xor(mine, 32);  // rows m and m^8 sit in lanes l and l^32
-    const int m = 4 * lq + r;
-    const int fi = i0 + (m & 7);
-    const bool first = m < 8;  // this lane holds x_fi (else x_{fi+DG/2})
-    float olo, ohi;
-    rope_pair(pos, p.freqs.w[fi], first ? mine : other, first ? other : mine, &olo, &ohi);
-    if (bvalid)
-      p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + (first ? fi : half + fi)] =
-          first ? olo : ohi;
-  }
+  const float other = __shfl_xor(mine, 32);  // rows m and m^8 sit in lanes l and l^32
+  const int m = 4 * lq + r;
+  const int fi = i0 + (m & 7);
+  const bool first = m < 8;  // this lane holds x_fi (else x_{fi+DG/2})
+  float olo, ohi;
+  rope_pair(pos, wf, first ? mine : other, first ? other : mine, &olo, &ohi);
+  if (bvalid)
+    p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + (first ? fi : half + fi)] =
+        first ? olo : ohi;
 }
 
 template <int D, int DG>
@@ -188,27 +185,51 @@ struct GateParams {
   float inv_sqrt_dg;
 };
 
-// One 512-thread workgroup per (sequence, KV head): its cache rows are all
-// requested at once (16-byte pieces, DG/8 lanes per row), dotted with the
-// gate query, and -- in the fused step -- selected on by the whole
-// workgroup without leaving LDS.
+// Part m (0, 1, 2) of the exact three-way bf16 split x = q0 + q1 + q2 (+ a
+// remainder below 2^-24 |x|): q0 = bf16(x), q1 = bf16(x - q0), q2 =
+// bf16(x - q0 - q1).  Each subtraction is exact in float32 (the operands
+// agree in their leading bits).
+__device__ __forceinline__ uint32_t bf16_part(float x, int m) {
+  const uint16_t h0 = f2bf(x);
+  const float r1 = x - __uint_as_float(static_cast<uint32_t>(h0) << 16);
+  const uint16_t h1 = f2bf(r1);
+  const float r2 = r1 - __uint_as_float(static_cast<uint32_t>(h1) << 16);
+  const uint16_t h2 = f2bf(r2);
+  return m == 0 ? h0 : (m == 1 ? h1 : h2);
+}
+
+// One 512-thread workgroup per (sequence, KV head); wave w scores 64 rows of
+// each 512-row pass.  A 16-column MFMA tile covers 16/P cache rows split
+// into their P = d_gate/32 parts of 32 dims: column n is (row n/P, part
+// n%P), so lane l's B operand is the 16 bytes at 64(l%16) + 16(l/16) of
+// 1 KiB of consecutive rows -- every load instruction reads one contiguous
+// 1 KiB.  A row m = 4p + c holds part p of the float32 gate query's exact
+// three-way bf16 split (component c < 3).  The diagonal lanes (lane group
+// l/16 == n%P) then receive the part's three component dot products in
+// elements 0..2: bf16 x bf16 products are exact in float32 and the three
+// components carry 24 bits of the query, so the logits keep float32
+// accuracy.  Each row's P part sums meet in LDS and are added in part
+// order.  In the fused step the workgroup then selects on the logits
+// without them leaving LDS.
 template <int DG>
 __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
-  constexpr int LPR = DG / 8;                    // lanes per cache row
-  constexpr int RPI = 64 / LPR;                  // rows per wave load
-  constexpr int RPL = kGateThreads / 64 * RPI;   // rows per workgroup load
-  constexpr int NL = kGateRows / RPL;            // loads per lane per pass
+  constexpr int P = DG / 32;                               // 32-dim parts of a row
+  constexpr int RPT = 16 / P;                              // rows per MFMA tile
+  constexpr int RPW = kGateRows / (kGateThreads / 64);     // rows per wave and pass (64)
+  constexpr int TPW = RPW / RPT;                           // tiles per wave and pass
+  static_assert(RPW == 64, "one row per lane in the part sum");
 
   extern __shared__ uint32_t s_keys[];           // NBmax logits (float bits)
   __shared__ SelectSmem s_sel;
+  __shared__ float s_part[kGateRows][4];         // part sums of one pass
 
   const int pair = blockIdx.x;
   const int b = pair / p.Hkv;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int c = lane % LPR;
-  const int rsub = lane / LPR;
+  const int n = lane & 15;
+  const int g = lane >> 4;
 
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.Lmax);
@@ -216,33 +237,50 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   nc = min(min(max(nc, 0), p.NBmax) + p.pending_new, L / p.BS);  // scored blocks
   if (tid < 256) s_sel.hist[tid] = 0;
 
-  const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 8 * c;
+  const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 32 * n + 8 * g;
   float* lo = p.logits_out ? p.logits_out + static_cast<int64_t>(pair) * p.NBmax : nullptr;
   const int passes = max(1, (nc + kGateRows - 1) / kGateRows);
-  float qv[8];
+  const bool diag = (g < P) && (g == n % P);
+  uint4 qa = make_uint4(0u, 0u, 0u, 0u);
   for (int pass = 0; pass < passes; ++pass) {
-    const int base = pass * kGateRows;
-    uint4 kv[NL];
+    const int row0 = pass * kGateRows + w * RPW;  // first row of this wave
+    uint4 kv[TPW];
 #pragma unroll
-    for (int it = 0; it < NL; ++it) {
-      const int j = base + it * RPL + w * RPI + rsub;
-      kv[it] = (j < nc) ? ld16(kc + static_cast<int64_t>(j) * DG) : make_uint4(0u, 0u, 0u, 0u);
+    for (int t = 0; t < TPW; ++t) {
+      const int j = row0 + t * RPT + n / P;  // the row this lane's piece belongs to
+      kv[t] = (j < nc) ? ld16(kc + static_cast<int64_t>(row0 + t * RPT) * DG)
+                       : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (pass == 0) {  // the gate query, while the first rows are in flight
-      const float4* qp = reinterpret_cast<const float4*>(p.q_gate + static_cast<int64_t>(pair) * DG + 8 * c);
-      const float4 a = qp[0], bb = qp[1];
-      qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
-      qv[4] = bb.x; qv[5] = bb.y; qv[6] = bb.z; qv[7] = bb.w;
-    }
-#pragma unroll
-    for (int it = 0; it < NL; ++it) {
-      const int j = base + it * RPL + w * RPI + rsub;
-      const float zj = logit_dot<DG>(qv, kv[it]) * p.inv_sqrt_dg;
-      if (c == 0 && j < p.NBmax) {
-        if (j < nc) s_keys[j] = __float_as_uint(zj);
-        if (lo != nullptr) lo[j] = (j < nc) ? zj : -INFINITY;
+    if (pass == 0) {  // the query parts, while the first rows are in flight
+      const int pa = n >> 2;
+      const int ca = n & 3;
+      if (pa < P && ca < 3) {
+        const float* qg = p.q_gate + static_cast<int64_t>(pair) * DG + 32 * pa + 8 * g;
+        const float4 x0 = *reinterpret_cast<const float4*>(qg);
+        const float4 x1 = *reinterpret_cast<const float4*>(qg + 4);
+        qa.x = bf16_part(x0.x, ca) | (bf16_part(x0.y, ca) << 16);
+        qa.y = bf16_part(x0.z, ca) | (bf16_part(x0.w, ca) << 16);
+        qa.z = bf16_part(x1.x, ca) | (bf16_part(x1.y, ca) << 16);
+        qa.w = bf16_part(x1.z, ca) | (bf16_part(x1.w, ca) << 16);
       }
     }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const f32x4_t acc = mfma16x16x32(qa, kv[t], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if (diag) s_part[w * RPW + t * RPT + n / P][g] = (acc[0] + acc[1]) + acc[2];
+    }
+    wave_lds_order();
+    {  // lane l: row row0 + l
+      const int j = row0 + lane;
+      const float* pp = s_part[w * RPW + lane];
+      float z = pp[0];
+#pragma unroll
+      for (int q = 1; q < P; ++q) z += pp[q];
+      z *= p.inv_sqrt_dg;
+      if (j < nc) s_keys[j] = __float_as_uint(z);
+      if (lo != nullptr && j < p.NBmax) lo[j] = (j < nc) ? z : -INFINITY;
+    }
+    wave_lds_order();  // the next pass rewrites this wave's part sums
   }
   if (lo != nullptr)  // rows past the passes walked above
     for (int j = passes * kGateRows + tid; j < p.NBmax; j += kGateThreads) lo[j] = -INFINITY;

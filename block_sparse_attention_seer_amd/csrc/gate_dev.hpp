@@ -73,6 +73,7 @@ __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* 
   constexpr int CP = CompressSmem<D, DG>::CP;
   constexpr int NTG = CompressSmem<D, DG>::NTG;
   const int tid = threadIdx.x;
+  const double wf = freqs.w[tid % (DG / 2)];  // requested early, used by the rotation
   if (tid < 256) {
     const int cp = tid % CP;
     const int tg = tid / CP;
@@ -120,27 +121,10 @@ __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* 
   __syncthreads();
   if (tid < DG / 2) {
     float olo, ohi;
-    rope_pair(static_cast<double>(j) * BS, freqs.w[tid], sm.v[tid], sm.v[tid + DG / 2], &olo, &ohi);
+    rope_pair(static_cast<double>(j) * BS, wf, sm.v[tid], sm.v[tid + DG / 2], &olo, &ohi);
     dst[tid] = f2bf(olo);
     dst[tid + DG / 2] = f2bf(ohi);
   }
-}
-
-// Dot product of a gate query (8 float values per lane, lanes of a row
-// group of DG/8 lanes) with one bf16 cache row piece, reduced over the row
-// group; every lane of the group ends with the sum.
-template <int DG>
-__device__ __forceinline__ float logit_dot(const float (&qv)[8], uint4 u) {
-  constexpr int LPR = DG / 8;
-  float s = bf_lo(u.x) * qv[0];
-  s = fmaf(bf_hi(u.x), qv[1], s);
-  s = fmaf(bf_lo(u.y), qv[2], s);
-  s = fmaf(bf_hi(u.y), qv[3], s);
-  s = fmaf(bf_lo(u.z), qv[4], s);
-  s = fmaf(bf_hi(u.z), qv[5], s);
-  s = fmaf(bf_lo(u.w), qv[6], s);
-  s = fmaf(bf_hi(u.w), qv[7], s);
-  return group_sum<LPR>(s);
 }
 
 }  // namespace seer

@@ -134,6 +134,15 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
   return min(min(lane_u32(v, 0), lane_u32(v, 16)), min(lane_u32(v, 32), lane_u32(v, 48)));
 }
 
+// Orders the LDS accesses of one wave: the ones before complete before the
+// ones after (a wave's LDS operations are performed in issue order; this
+// keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within
 // each row, then row 0's total into row 1 (and row 2's into row 3), then
 // the first two rows' total into rows 2 and 3.

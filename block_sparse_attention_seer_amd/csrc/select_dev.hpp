@@ -8,9 +8,11 @@
 // multiple of b the incomplete last block is always selected.
 // [CP Knowl 6]: the index tensor is [batch, heads_kv, max_selected_blocks].
 //
-// The whole workgroup selects; thread t owns a contiguous range of block
-// indices, so a workgroup prefix sum over per-thread counts writes the
-// selected indices in ascending order without a sort.
+// NT threads select (a whole 512-thread workgroup in the kernels here, so
+// that each thread holds one key at the usual sizes; with NT = 64 one wave
+// selects without workgroup barriers); thread t owns a contiguous range of
+// block indices, so a prefix sum over per-thread counts writes the selected
+// indices in ascending order without a sort.
 //
 // Top-k is an exact selection by narrowing: the keys still "in play" always
 // form one interval [lo, hi] of the order-preserving 32-bit key (every key
@@ -40,7 +42,19 @@ struct SelectSmem {
   int pick[3];
 };
 
-// Exclusive prefix sum of v over the workgroup in thread order, and the
+// Makes the LDS writes of the NT selecting threads visible to all of them:
+// a workgroup barrier, or for a single wave only an ordering point (the LDS
+// operations of one wave complete in issue order).
+template <int NT>
+__device__ __forceinline__ void sel_sync() {
+  if constexpr (NT == 64) {
+    wave_lds_order();
+  } else {
+    __syncthreads();
+  }
+}
+
+// Exclusive prefix sum of v over the NT threads in thread order, and the
 // total.  `part` (NT/64 ints of LDS) must not be in use by another scan
 // that some thread may still be reading.
 template <int NT>
@@ -49,6 +63,10 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* part, int* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int incl = wave_inclusive_scan(v);
+  if constexpr (NW == 1) {
+    *total = __builtin_amdgcn_readlane(incl, 63);
+    return incl - v;
+  }
   if (lane == 63) part[w] = incl;
   __syncthreads();
   int before = 0, tot = 0;
@@ -68,6 +86,7 @@ __device__ __forceinline__ void wg_minmax_f(float& mn, float& mx, SelectSmem& sm
   const int w = threadIdx.x >> 6;
   mn = wave_min(mn);
   mx = wave_max(mx);
+  if constexpr (NW == 1) return;
   if ((threadIdx.x & 63) == 0) {
     sm.fred[0][w] = mn;
     sm.fred[1][w] = mx;
@@ -88,6 +107,7 @@ __device__ __forceinline__ void wg_minmax_u(uint32_t& mn, uint32_t& mx, SelectSm
   const int w = threadIdx.x >> 6;
   mn = wave_umin(mn);
   mx = wave_umax(mx);
+  if constexpr (NW == 1) return;
   if ((threadIdx.x & 63) == 0) {
     sm.ured[0][w] = mn;
     sm.ured[1][w] = mx;
@@ -109,7 +129,7 @@ __device__ __forceinline__ void wg_minmax_u(uint32_t& mn, uint32_t& mx, SelectSm
 template <int NT>
 __device__ __forceinline__ void hist_pick(SelectSmem& sm, int need, int& bucket, int& above,
                                           int& count) {
-  __syncthreads();
+  sel_sync<NT>();
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
     int hb[4];
@@ -136,28 +156,53 @@ __device__ __forceinline__ void hist_pick(SelectSmem& sm, int need, int& bucket,
       }
     }
   }
-  __syncthreads();
+  sel_sync<NT>();
   bucket = sm.pick[0];
   above = sm.pick[1];
   count = sm.pick[2];
 }
 
-// Called by all NT threads of the workgroup once keys[0..nc) (LDS, the
-// logits as float bits) are visible to every thread.  sm.hist must be zero
-// on entry and is left zero.  Appends the unscored blocks nc ..
-// total_blocks-1 and writes the ascending, -1 padded row out[0..max_sel)
-// plus its count.
-template <int NT>
-__device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSmem& sm, int nc,
-                                                 int total_blocks, int mode, int topk,
-                                                 float log_tau, int max_sel, int32_t* out,
-                                                 int32_t* count_out) {
+// The keys j0 .. j0+n-1 of one thread: held in registers when KPL > 0 (n <=
+// KPL), else read from LDS on every visit.  each(f) calls f(j, z) in index
+// order.
+template <int KPL>
+struct KeyRange {
+  const uint32_t* keys;
+  int j0, n;
+  float zr[KPL > 0 ? KPL : 1];
+  __device__ __forceinline__ KeyRange(const uint32_t* k, int first, int count)
+      : keys(k), j0(first), n(count) {
+    if constexpr (KPL > 0) {
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) zr[i] = (i < n) ? __uint_as_float(keys[j0 + i]) : 0.f;
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    if constexpr (KPL > 0) {
+#pragma unroll
+      for (int i = 0; i < KPL; ++i)
+        if (i < n) f(j0 + i, zr[i]);
+    } else {
+      for (int i = 0; i < n; ++i) f(j0 + i, __uint_as_float(keys[j0 + i]));
+    }
+  }
+};
+
+// The selection proper; KPL as in KeyRange (all NT threads take the same
+// instantiation).
+template <int NT, int KPL>
+__device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectSmem& sm, int nc,
+                                                   int total_blocks, int mode, int topk,
+                                                   float log_tau, int max_sel, int32_t* out,
+                                                   int32_t* count_out) {
   static_assert(NT % 64 == 0 && NT / 64 <= kSelMaxWaves, "workgroup size");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int vpt = (nc + NT - 1) / NT;
   const int j0 = min(nc, tid * vpt);
   const int j1 = min(nc, j0 + vpt);
+  const KeyRange<KPL> kr(keys, j0, j1 - j0);
 
   // A key is taken iff  key > lo, or key == lo and (whole || rank < need)
   // (top-k), or z > thr (threshold); `all` / `none` short-cut both.
@@ -176,55 +221,49 @@ __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSme
       need = k;
       int m = nc;  // keys in play
       float zmn = INFINITY, zmx = -INFINITY;
-      for (int j = j0; j < j1; ++j) {
-        const float z = __uint_as_float(keys[j]);
+      kr.each([&](int, float z) {
         zmn = fminf(zmn, z);
         zmx = fmaxf(zmx, z);
-      }
+      });
       wg_minmax_f<NT>(zmn, zmx, sm);
       const float scale = 256.f / (zmx - zmn);
       uint32_t hi;
+      uint32_t kmn = 0xffffffffu, kmx = 0u;
       if (zmx > zmn && scale > 0.f && scale < INFINITY) {
         // linear buckets on the value; monotone in z (NaN counts lowest)
         auto fbucket = [&](float z) -> int {
           return (z == z) ? min(255, static_cast<int>((z - zmn) * scale)) : 0;
         };
-        for (int j = j0; j < j1; ++j) atomicAdd(&sm.hist[fbucket(__uint_as_float(keys[j]))], 1);
+        kr.each([&](int, float z) { atomicAdd(&sm.hist[fbucket(z)], 1); });
         int b, above;
         hist_pick<NT>(sm, need, b, above, m);
         need -= above;
         // the kept bucket as an interval of keys
-        uint32_t kmn = 0xffffffffu, kmx = 0u;
-        for (int j = j0; j < j1; ++j) {
-          const float z = __uint_as_float(keys[j]);
+        kr.each([&](int, float z) {
           if (fbucket(z) == b) {
             const uint32_t key = float_key(z);
             kmn = min(kmn, key);
             kmx = max(kmx, key);
           }
-        }
-        wg_minmax_u<NT>(kmn, kmx, sm);
-        lo = kmn;
-        hi = kmx;
+        });
       } else {
-        uint32_t kmn = 0xffffffffu, kmx = 0u;
-        for (int j = j0; j < j1; ++j) {
-          const uint32_t key = float_key(__uint_as_float(keys[j]));
+        kr.each([&](int, float z) {
+          const uint32_t key = float_key(z);
           kmn = min(kmn, key);
           kmx = max(kmx, key);
-        }
-        wg_minmax_u<NT>(kmn, kmx, sm);
-        lo = kmn;
-        hi = kmx;
+        });
       }
+      wg_minmax_u<NT>(kmn, kmx, sm);
+      lo = kmn;
+      hi = kmx;
       // narrow on key bits until the kept bucket is taken whole or is a
       // single value
       while (m != need && lo != hi) {
         const int shift = max(0, 32 - __clz(static_cast<int>(hi - lo)) - 8);
-        for (int j = j0; j < j1; ++j) {
-          const uint32_t key = float_key(__uint_as_float(keys[j]));
+        kr.each([&](int, float z) {
+          const uint32_t key = float_key(z);
           if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> shift], 1);
-        }
+        });
         int b, above;
         hist_pick<NT>(sm, need, b, above, m);
         need -= above;
@@ -238,22 +277,25 @@ __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSme
   } else {
     // softmax_j > tau  <=>  z_j > ln(tau) + logsumexp(z); fixed summation order
     float mx = -INFINITY;
-    for (int j = j0; j < j1; ++j) mx = fmaxf(mx, __uint_as_float(keys[j]));
+    kr.each([&](int, float z) { mx = fmaxf(mx, z); });
     mx = wave_max(mx);
-    if ((tid & 63) == 0) sm.fred[0][tid >> 6] = mx;
-    __syncthreads();
-    mx = sm.fred[0][0];
+    if constexpr (NW > 1) {
+      if ((tid & 63) == 0) sm.fred[0][tid >> 6] = mx;
+      __syncthreads();
+      mx = sm.fred[0][0];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) mx = fmaxf(mx, sm.fred[0][i]);
+      for (int i = 1; i < NW; ++i) mx = fmaxf(mx, sm.fred[0][i]);
+    }
     float se = 0.f;
-    if (nc > 0)
-      for (int j = j0; j < j1; ++j) se += expf(__uint_as_float(keys[j]) - mx);
+    kr.each([&](int, float z) { se += expf(z - mx); });
     se = wave_sum(se);
-    if ((tid & 63) == 0) sm.fred[1][tid >> 6] = se;
-    __syncthreads();
-    se = sm.fred[1][0];
+    if constexpr (NW > 1) {
+      if ((tid & 63) == 0) sm.fred[1][tid >> 6] = se;
+      __syncthreads();
+      se = sm.fred[1][0];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) se += sm.fred[1][i];
+      for (int i = 1; i < NW; ++i) se += sm.fred[1][i];
+    }
     thr = (nc > 0) ? log_tau + (mx + logf(se)) : INFINITY;
   }
 
@@ -262,15 +304,15 @@ __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSme
   int eq_before = 0;
   if (topk_range && !whole) {
     int eq = 0;
-    for (int j = j0; j < j1; ++j) eq += (float_key(__uint_as_float(keys[j])) == lo);
+    kr.each([&](int, float z) { eq += (float_key(z) == lo); });
     int unused;
     eq_before = wg_exclusive_scan<NT>(eq, sm.scan[0], &unused);
   }
-  auto taken = [&](int j, int& rank) -> bool {
-    if (mode != SEER_SELECT_TOPK) return __uint_as_float(keys[j]) > thr;
+  auto taken = [&](float z, int& rank) -> bool {
+    if (mode != SEER_SELECT_TOPK) return z > thr;
     if (all) return true;
     if (none) return false;
-    const uint32_t key = float_key(__uint_as_float(keys[j]));
+    const uint32_t key = float_key(z);
     if (key > lo) return true;
     if (key < lo) return false;
     const bool t = whole || rank < need;
@@ -280,18 +322,18 @@ __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSme
   int nsel = 0;
   {
     int rank = eq_before;
-    for (int j = j0; j < j1; ++j) nsel += taken(j, rank);
+    kr.each([&](int, float z) { nsel += taken(z, rank); });
   }
   int scored_total;
   int pos = wg_exclusive_scan<NT>(nsel, sm.scan[1], &scored_total);
   {
     int rank = eq_before;
-    for (int j = j0; j < j1; ++j) {
-      if (taken(j, rank)) {
+    kr.each([&](int j, float z) {
+      if (taken(z, rank)) {
         if (pos < max_sel) out[pos] = j;
         ++pos;
       }
-    }
+    });
   }
   // blocks without a cache entry (normally the partial block) are forced
   const int forced = max(0, total_blocks - nc);
@@ -302,6 +344,31 @@ __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSme
   const int written = min(scored_total + forced, max_sel);
   for (int i = written + tid; i < max_sel; i += NT) out[i] = -1;
   if (tid == 0) *count_out = written;
+}
+
+// Called by all NT threads once keys[0..nc) (LDS, the logits as float bits)
+// are visible to every one of them.  sm.hist must be zero on entry and is
+// left zero.  Appends the unscored blocks nc .. total_blocks-1 and writes the
+// ascending, -1 padded row out[0..max_sel) plus its count.  Up to 32 keys
+// per thread are held in registers.
+template <int NT>
+__device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSmem& sm, int nc,
+                                                 int total_blocks, int mode, int topk,
+                                                 float log_tau, int max_sel, int32_t* out,
+                                                 int32_t* count_out) {
+  const int vpt = (nc + NT - 1) / NT;
+  if (vpt <= 1)
+    select_blocks_impl<NT, 1>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
+                              count_out);
+  else if (vpt <= 8)
+    select_blocks_impl<NT, 8>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
+                              count_out);
+  else if (vpt <= 32)
+    select_blocks_impl<NT, 32>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
+                               count_out);
+  else
+    select_blocks_impl<NT, 0>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
+                              count_out);
 }
 
 }  // namespace seer
