@@ -559,3 +559,69 @@ def test_fused_pipeline_steps_match_oracle(S):
             for b in range(w.batch):
                 for h in (0, w.num_kv_heads - 1):
                     _check_pair(w, inp, st, b, h, f"fused pipeline step={step} b={b} h={h}")
+
+
+# ------------------------------------------- full sizes, fused launch config
+
+@pytest.mark.parametrize("name,pairs", [("qwen3_14b_b16", 12), ("qwen3_8b_layer", 8)])
+def test_fused_step_full_size_sampled(S, name, pairs):
+    """The fused step exactly as bench.py launches it (all automatic split
+    and workgroup choices, logits not kept) at the workload's full size."""
+    w = WORKLOADS[name]
+    say(f"fused full size {name}: generating inputs")
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    seq = inp["seq_lens"]
+    st.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq,
+                  keep_logits=False)
+    torch.cuda.synchronize()
+    say(f"fused full size {name}: checking")
+    assert st.kcomp_lens.cpu().tolist() == [int(L) // w.block_size for L in seq.cpu()]
+    all_pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    rng = np.random.default_rng(1)
+    sample = [all_pairs[i] for i in rng.choice(len(all_pairs), size=min(pairs, len(all_pairs)),
+                                               replace=False)]
+    for b, h in sample:
+        _check_pair(w, inp, st, b, h, f"fused {name} b={b} h={h}")
+    assert torch.isfinite(st.out.float()).all() and torch.isfinite(st.lse).all()
+    # every (b, h) selected exactly k blocks (L is a multiple of b: no partial block)
+    assert bool((st.num_selected == w.topk_blocks).all())
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_pipeline_full_size_sampled(S):
+    """The 128k pipeline workload at full size (32 sequences, lengths up to
+    131072): bulk cache build, then fused steps with appends, checking sampled
+    pairs -- including every sequence that completed a block -- after the
+    last step."""
+    from workloads import append_token
+    w = WORKLOADS["pipeline_128k"]
+    steps = 3
+    say("pipeline full size: generating inputs")
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    start = inp["seq_lens"].cpu().clone()
+    gen = torch.Generator(device=DEV).manual_seed(79)
+    for step in range(steps):
+        append_token(inp, gen)
+        st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+                      inp["seq_lens"], keep_logits=False)
+    torch.cuda.synchronize()
+    say("pipeline full size: checking")
+    now = inp["seq_lens"].cpu()
+    assert st.kcomp_lens.cpu().tolist() == [int(L) // w.block_size for L in now]
+    grew = [b for b in range(w.batch) if int(now[b]) // 64 != int(start[b]) // 64]
+    rng = np.random.default_rng(2)
+    seqs = sorted(set(grew[:3]) | set(rng.choice(w.batch, size=3, replace=False).tolist()))
+    for b in seqs:
+        for h in (0, w.num_kv_heads - 1):
+            _check_pair(w, inp, st, b, h, f"pipeline full b={b} h={h} L={int(now[b])}")
+    del inp
+    torch.cuda.empty_cache()
