@@ -9,17 +9,16 @@
 // block, once every b tokens; top-k or threshold then picks the blocks.
 //
 // Kernels:
-//   prep_kernel    one launch for two kinds of independent tasks:
-//                  * gate-query tiles: 16 gate rows x 16 sequences of one KV
-//                    head as an MFMA GEMM (W_q read once per step, not once
-//                    per sequence), the g*d contraction split over 4 waves
-//                    with every load issued up front, then RoPE in float64;
-//                  * cache-entry tasks: one newly completed block of one
-//                    (sequence, KV head) each (pool, W_k GEMV, RoPE, bf16).
-//   gate_kernel    one 512-thread workgroup per (sequence, KV head): all its
-//                  cache rows requested at once, block logits in float32,
-//                  and -- in the fused step -- the selection, from LDS.
+//   prep_kernel    cache-entry tasks of the staged update: one newly
+//                  completed block of one (sequence, KV head) each (pool,
+//                  W_k GEMV, RoPE, bf16).
 //   commit_kernel  raises kcomp_lens once every new entry is written.
+//   gate_kernel    one 512-thread workgroup per (sequence, KV head): the
+//                  pair's new cache entries (fused step), its gate query
+//                  (MFMA GEMV + RoPE), its block logits (MFMA) and -- in the
+//                  fused step -- the selection, all without leaving the
+//                  workgroup.  Every global load it needs is issued at its
+//                  start, so the W_q, query and cache-row latencies overlap.
 #include <cmath>
 
 #include "gate_dev.hpp"
@@ -45,15 +44,10 @@ int check_launch(const char* what) {
   return SEER_OK;
 }
 
-// ------------------------------------------------ gate query + cache entries
+// ------------------------------------------------------- staged cache update
 
 struct PrepParams {
-  // gate-query tiles (n_query_wgs of them, first in the grid)
-  const uint16_t* q_nope;
-  const uint16_t* w_q;
-  float* q_gate;
-  int n_query_wgs;
-  // cache-entry tasks (the rest of the grid): entry kcomp_lens[b] + z
+  // entry kcomp_lens[b] + z of pair (b, h) for workgroup pair * max_new + z
   const uint16_t* k_nope;
   const uint16_t* w_k;
   const int32_t* kcomp_lens;
@@ -61,87 +55,14 @@ struct PrepParams {
   int max_new;
   const int32_t* seq_lens;
   int64_t sb, sh, st;
-  int B, Hq, Hkv, G, BS, Lmax, NBmax;
+  int Hkv, BS, Lmax, NBmax;
   RopeFreqs freqs;
 };
 
-constexpr int kQueryStepsPerWave = 16;  // k-steps of 32 per wave: g*d <= 2048
-
-// Gate-query tile t: 16 gate rows (rows i0..i0+7 and their RoPE partners
-// i0+DG/2..) x 16 sequences of one KV head as MFMA D = W_q . X.  The 4 waves
-// split the g*d contraction; each issues all of its loads before its first
-// MFMA; the partial tiles are summed in a fixed order, and wave w rotates
-// and stores element w of every lane's accumulator.
-template <int D, int DG>
-__device__ void query_tile(const PrepParams& p, int t, float (*red)[64][4]) {
-  const int RT = DG / 16;
-  const int BT = (p.B + 15) / 16;
-  const int h = t / (RT * BT);
-  const int rt = (t / BT) % RT;
-  const int b0 = (t % BT) * 16;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int ln = lane & 15;
-  const int lq = lane >> 4;
-  const int half = DG / 2;
-  const int i0 = rt * 8;
-  const int K = p.G * D;
-  const int KST = K / 32;
-
-  const int bq = b0 + ln;
-  const bool bvalid = bq < p.B;
-  int L = bvalid ? p.seq_lens[bq] : 1;  // issued early; used by the rotation
-  // frequency of the row this lane rotates (element w of its tile column), also early
-  const double wf = p.freqs.w[i0 + ((4 * lq + w) & 7)];
-
-  const int arow = (ln < 8) ? (i0 + ln) : (half + i0 + ln - 8);
-  const uint16_t* wrow = p.w_q + (static_cast<int64_t>(h) * DG + arow) * K + 8 * lq;
-  const uint16_t* xrow = p.q_nope + (static_cast<int64_t>(bvalid ? bq : 0) * p.Hq + h * p.G) * D + 8 * lq;
-  const int s0 = w * KST / 4;
-  const int s1 = (w + 1) * KST / 4;
-  uint4 a[kQueryStepsPerWave], x[kQueryStepsPerWave];
-#pragma unroll
-  for (int i = 0; i < kQueryStepsPerWave; ++i) {
-    const int s = s0 + i;
-    a[i] = (s < s1) ? ld16(wrow + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
-    x[i] = (s < s1 && bvalid) ? ld16(xrow + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < kQueryStepsPerWave; ++i)
-    if (s0 + i < s1) acc = mfma16x16x32(a[i], x[i], acc);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) red[w][lane][r] = acc[r];
-  __syncthreads();
-  // wave w finishes element r = w of every lane: Y[tile row 4*lq + w][sequence b0 + ln]
-  const int r = w;
-  const float mine = ((red[0][lane][r] + red[1][lane][r]) + red[2][lane][r]) + red[3][lane][r];
-  L = min(max(L, 0), p.Lmax);
-  const double pos = static_cast<double>(L - 1);
-  const float other = __shfl_xor(mine, 32);  // rows m and m^8 sit in lanes l and l^32
-  const int m = 4 * lq + r;
-  const int fi = i0 + (m & 7);
-  const bool first = m < 8;  // this lane holds x_fi (else x_{fi+DG/2})
-  float olo, ohi;
-  rope_pair(pos, wf, first ? mine : other, first ? other : mine, &olo, &ohi);
-  if (bvalid)
-    p.q_gate[(static_cast<int64_t>(bq) * p.Hkv + h) * DG + (first ? fi : half + fi)] =
-        first ? olo : ohi;
-}
-
 template <int D, int DG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
-  __shared__ union {
-    float red[4][64][4];
-    CompressSmem<D, DG> cm;
-  } sm;
-  const int t = blockIdx.x;
-  if (t < p.n_query_wgs) {
-    query_tile<D, DG>(p, t, sm.red);
-    return;
-  }
-  const int c = t - p.n_query_wgs;
+  __shared__ CompressSmem<D, DG> cm;
+  const int c = blockIdx.x;
   const int pair = c / p.max_new;
   const int z = c - pair * p.max_new;
   const int b = pair / p.Hkv;
@@ -152,10 +73,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
   cl = min(max(cl, 0), p.NBmax);
   const int j = cl + z;
   if (j >= L / p.BS) return;  // uniform over the workgroup
+  const double wf = p.freqs.w[threadIdx.x % (DG / 2)];
   const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j) * p.BS * p.st;
   uint16_t* dst = p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j) * DG;
-  compress_block<D, DG>(sm.cm, keys, p.st, p.BS, p.w_k + static_cast<int64_t>(h) * DG * 3 * D,
-                        p.freqs, j, dst);
+  compress_block<D, DG>(cm, keys, p.st, p.BS, p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf, j,
+                        dst);
 }
 
 __global__ void commit_kernel(const int32_t* seq_lens, int32_t* kcomp_lens, int B, int BS, int Lmax,
@@ -165,24 +87,38 @@ __global__ void commit_kernel(const int32_t* seq_lens, int32_t* kcomp_lens, int 
   kcomp_lens[b] = committed_count(seq_lens[b], kcomp_lens[b], BS, Lmax, NBmax, max_new);
 }
 
+template <int D, int DG>
+void launch_prep_t(const PrepParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((prep_kernel<D, DG>), dim3(grid), dim3(256), 0, s, p);
+}
+
 // ------------------------------------------------------------------ gate
 
 constexpr int kGateThreads = 512;
-constexpr int kGateRows = 512;  // cache rows per prefetch pass
+constexpr int kGateRows = 512;   // cache rows per prefetch pass
+constexpr int kQueryChunks = 5;  // 128-dim chunks of g*d per W_q load group
 
 struct GateParams {
-  const float* q_gate;          // [B, H_kv, d_gate]
-  const uint16_t* kcomp;
+  const uint16_t* q_nope;  // [B, H_q, d]
+  const uint16_t* w_q;     // [H_kv, d_gate, g*d]
+  float* q_gate_out;       // [B, H_kv, d_gate] or null
+  // new cache entries of this launch (fused step): entries c .. c+nnew-1
+  // with nnew = min(floor(L/b), c + max_new) - c, c = kcomp_lens[b]
+  const uint16_t* k_nope;
+  const uint16_t* w_k;
+  int64_t sb, sh, st;
+  int max_new;
+  uint16_t* kcomp;
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
-  float* logits_out;            // [B, H_kv, NBmax] or null
-  int32_t* block_idx;           // select when non-null
+  float* logits_out;   // [B, H_kv, NBmax] or null
+  int32_t* block_idx;  // select when non-null
   int32_t* num_selected;
-  int pending_new;              // entries appended this step, not yet counted
-  int Hkv, BS, Lmax, NBmax;
+  int Hq, Hkv, G, BS, Lmax, NBmax;
   int mode, topk, max_sel;
   float log_tau;
   float inv_sqrt_dg;
+  RopeFreqs freqs;
 };
 
 // Part m (0, 1, 2) of the exact three-way bf16 split x = q0 + q1 + q2 (+ a
@@ -198,33 +134,77 @@ __device__ __forceinline__ uint32_t bf16_part(float x, int m) {
   return m == 0 ? h0 : (m == 1 ? h1 : h2);
 }
 
-// One 512-thread workgroup per (sequence, KV head); wave w scores 64 rows of
-// each 512-row pass.  A 16-column MFMA tile covers 16/P cache rows split
-// into their P = d_gate/32 parts of 32 dims: column n is (row n/P, part
-// n%P), so lane l's B operand is the 16 bytes at 64(l%16) + 16(l/16) of
-// 1 KiB of consecutive rows -- every load instruction reads one contiguous
-// 1 KiB.  A row m = 4p + c holds part p of the float32 gate query's exact
-// three-way bf16 split (component c < 3).  The diagonal lanes (lane group
-// l/16 == n%P) then receive the part's three component dot products in
-// elements 0..2: bf16 x bf16 products are exact in float32 and the three
-// components carry 24 bits of the query, so the logits keep float32
-// accuracy.  Each row's P part sums meet in LDS and are added in part
-// order.  In the fused step the workgroup then selects on the logits
-// without them leaving LDS.
-template <int DG>
+// Chunk group c0 .. c0+kQueryChunks-1 (128 dims each) of this lane's W_q
+// pieces (B operand, tiles of 4 rows) and query pieces (A operand).
+template <int TQ>
+__device__ __forceinline__ void load_query_group(uint4 (&wb)[TQ][kQueryChunks],
+                                                 uint4 (&xa)[kQueryChunks], const uint16_t* wq,
+                                                 const uint16_t* xq, int c0, int nch, int K,
+                                                 int n, int g, int w) {
+  const bool xlane = (n & 3) == 0;  // A row 4p holds part p = n/4 of the query heads
+#pragma unroll
+  for (int c = 0; c < kQueryChunks; ++c) {
+    const int k0 = (c0 + c) * 128;
+    const bool in = (c0 + c < nch) && (k0 + 32 * (n & 3) + 8 * g < K);
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) {
+      const int row = (w * TQ + t) * 4 + (n >> 2);
+      wb[t][c] = in ? ld16(wq + static_cast<int64_t>(row) * K + k0) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    xa[c] = (xlane && c0 + c < nch && k0 + 32 * (n >> 2) + 8 * g < K)
+                ? ld16(xq + k0)
+                : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// This lane's pieces of the cache rows of one pass that are already cached
+// (j < nc0); the rest are zero.
+template <int TPW, int RPT, int P, int DG>
+__device__ __forceinline__ void load_rows(uint4 (&kv)[TPW], const uint16_t* kc, int row0, int nc0,
+                                          int n) {
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int j = row0 + t * RPT + n / P;
+    kv[t] = (j < nc0) ? ld16(kc + static_cast<int64_t>(row0 + t * RPT) * DG)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// One 512-thread workgroup per (sequence, KV head).
+//
+// Both contractions use the same MFMA layout.  A 16-column tile covers
+// 16/P rows of a matrix, each split into P parts of 32 dims: column n is
+// (row n/P, part n%P), so lane l's B operand is the 16 bytes at
+// 64(l%16) + 16(l/16) of the tile's rows -- every load instruction reads
+// whole 256-byte runs.  A row m = 4p + c holds part p of the vector
+// (component c).  The diagonal lanes (lane group l/16 == n%P) receive each
+// part's dot products; a row's P part sums meet in LDS and are added in part
+// order.
+//   gate query: rows = W_q[h] rows, taken 128 dims (P = 4) at a time with
+//     the chunks' products accumulated in the MFMA; the vector is the bf16
+//     concatenation of the group's q_nope heads (component 0 only, exact);
+//   logits: rows = the pair's cache rows (P = d_gate/32); the vector is the
+//     float32 gate query split exactly into three bf16 components, so the
+//     logits keep float32 accuracy (bf16 x bf16 products are exact).
+template <int D, int DG>
 __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
-  constexpr int P = DG / 32;                               // 32-dim parts of a row
-  constexpr int RPT = 16 / P;                              // rows per MFMA tile
-  constexpr int RPW = kGateRows / (kGateThreads / 64);     // rows per wave and pass (64)
-  constexpr int TPW = RPW / RPT;                           // tiles per wave and pass
+  constexpr int P = DG / 32;                            // 32-dim parts of a cache row
+  constexpr int RPT = 16 / P;                           // cache rows per MFMA tile
+  constexpr int RPW = kGateRows / (kGateThreads / 64);  // cache rows per wave and pass (64)
+  constexpr int TPW = RPW / RPT;                        // logit tiles per wave and pass
+  constexpr int TQ = DG / 32;                           // W_q tiles (4 rows each) per wave
   static_assert(RPW == 64, "one row per lane in the part sum");
 
   extern __shared__ uint32_t s_keys[];           // NBmax logits (float bits)
   __shared__ SelectSmem s_sel;
-  __shared__ float s_part[kGateRows][4];         // part sums of one pass
+  __shared__ float s_part[kGateRows][4];         // part sums (gate query, then logits)
+  __shared__ float s_qg[DG];                     // the gate query
+  __shared__ uint16_t s_new[kMaxInlineNew][DG];  // this launch's new cache entries
+  __shared__ CompressSmem<D, DG> s_cm;
 
   const int pair = blockIdx.x;
   const int b = pair / p.Hkv;
+  const int h = pair - b * p.Hkv;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
@@ -233,35 +213,95 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
 
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.Lmax);
-  int nc = p.kcomp_lens[b];
-  nc = min(min(max(nc, 0), p.NBmax) + p.pending_new, L / p.BS);  // scored blocks
+  int nc0 = p.kcomp_lens[b];
+  nc0 = min(min(max(nc0, 0), p.NBmax), L / p.BS);  // cached blocks
+  const int nc = min(L / p.BS, nc0 + p.max_new);   // scored: with this launch's entries
+  const int nnew = nc - nc0;
   if (tid < 256) s_sel.hist[tid] = 0;
+  const double wf = p.freqs.w[tid % (DG / 2)];
+
+  // ---- all loads first: W_q rows and the query heads (first chunk group),
+  // then the first pass of cache rows
+  const int K = p.G * D;  // W_q row length
+  const int nch = (K + 127) / 128;
+  const uint16_t* wq = p.w_q + static_cast<int64_t>(h) * DG * K + 32 * (n & 3) + 8 * g;
+  const uint16_t* xq =
+      p.q_nope + (static_cast<int64_t>(b) * p.Hq + h * p.G) * D + 32 * (n >> 2) + 8 * g;
+  uint4 wb[TQ][kQueryChunks], xa[kQueryChunks];
+  load_query_group<TQ>(wb, xa, wq, xq, 0, nch, K, n, g, w);
 
   const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 32 * n + 8 * g;
-  float* lo = p.logits_out ? p.logits_out + static_cast<int64_t>(pair) * p.NBmax : nullptr;
   const int passes = max(1, (nc + kGateRows - 1) / kGateRows);
-  const bool diag = (g < P) && (g == n % P);
+  uint4 kv[TPW];  // rows already cached; this launch's entries come from LDS
+  load_rows<TPW, RPT, P, DG>(kv, kc, w * RPW, nc0, n);
+
+  // ---- new cache entries (blocks completed since the last update)
+  for (int e = 0; e < nnew; ++e) {
+    const int j = nc0 + e;
+    const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j) * p.BS * p.st;
+    compress_block<D, DG>(s_cm, keys, p.st, p.BS, p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf,
+                          j, p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j) * DG, s_new[e]);
+    __syncthreads();  // s_cm is reused by the next entry
+  }
+
+  // ---- gate query: y = W_q[h] x, then RoPE at position L-1
+  {
+    f32x4_t acc[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nch; c0 += kQueryChunks) {
+      if (c0 > 0) load_query_group<TQ>(wb, xa, wq, xq, c0, nch, K, n, g, w);
+#pragma unroll
+      for (int c = 0; c < kQueryChunks; ++c)
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) acc[t] = mfma16x16x32(xa[c], wb[t][c], acc[t]);
+    }
+    if (g == (n & 3)) {
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) s_part[(w * TQ + t) * 4 + (n >> 2)][g] = acc[t][0];
+    }
+  }
+  __syncthreads();
+  if (tid < DG / 2) {
+    const float* lo_row = s_part[tid];
+    const float* hi_row = s_part[tid + DG / 2];
+    const float ylo = ((lo_row[0] + lo_row[1]) + lo_row[2]) + lo_row[3];
+    const float yhi = ((hi_row[0] + hi_row[1]) + hi_row[2]) + hi_row[3];
+    float olo, ohi;
+    rope_pair(static_cast<double>(L - 1), wf, ylo, yhi, &olo, &ohi);
+    s_qg[tid] = olo;
+    s_qg[tid + DG / 2] = ohi;
+    if (p.q_gate_out != nullptr) {
+      p.q_gate_out[static_cast<int64_t>(pair) * DG + tid] = olo;
+      p.q_gate_out[static_cast<int64_t>(pair) * DG + tid + DG / 2] = ohi;
+    }
+  }
+  __syncthreads();
+
+  // ---- logits
   uint4 qa = make_uint4(0u, 0u, 0u, 0u);
+  {
+    const int pa = n >> 2;
+    const int ca = n & 3;
+    if (pa < P && ca < 3) {
+      const float* x = s_qg + 32 * pa + 8 * g;
+      qa.x = bf16_part(x[0], ca) | (bf16_part(x[1], ca) << 16);
+      qa.y = bf16_part(x[2], ca) | (bf16_part(x[3], ca) << 16);
+      qa.z = bf16_part(x[4], ca) | (bf16_part(x[5], ca) << 16);
+      qa.w = bf16_part(x[6], ca) | (bf16_part(x[7], ca) << 16);
+    }
+  }
+  const bool diag = (g < P) && (g == n % P);
+  float* lo = p.logits_out ? p.logits_out + static_cast<int64_t>(pair) * p.NBmax : nullptr;
   for (int pass = 0; pass < passes; ++pass) {
     const int row0 = pass * kGateRows + w * RPW;  // first row of this wave
-    uint4 kv[TPW];
+    if (pass > 0) load_rows<TPW, RPT, P, DG>(kv, kc, row0, nc0, n);
+    if (nnew > 0) {  // this launch's entries, from LDS
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int j = row0 + t * RPT + n / P;  // the row this lane's piece belongs to
-      kv[t] = (j < nc) ? ld16(kc + static_cast<int64_t>(row0 + t * RPT) * DG)
-                       : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (pass == 0) {  // the query parts, while the first rows are in flight
-      const int pa = n >> 2;
-      const int ca = n & 3;
-      if (pa < P && ca < 3) {
-        const float* qg = p.q_gate + static_cast<int64_t>(pair) * DG + 32 * pa + 8 * g;
-        const float4 x0 = *reinterpret_cast<const float4*>(qg);
-        const float4 x1 = *reinterpret_cast<const float4*>(qg + 4);
-        qa.x = bf16_part(x0.x, ca) | (bf16_part(x0.y, ca) << 16);
-        qa.y = bf16_part(x0.z, ca) | (bf16_part(x0.w, ca) << 16);
-        qa.z = bf16_part(x1.x, ca) | (bf16_part(x1.y, ca) << 16);
-        qa.w = bf16_part(x1.z, ca) | (bf16_part(x1.w, ca) << 16);
+      for (int t = 0; t < TPW; ++t) {
+        const int j = row0 + t * RPT + n / P;
+        if (j >= nc0 && j < nc)
+          kv[t] = *reinterpret_cast<const uint4*>(&s_new[j - nc0][32 * (n % P) + 8 * g]);
       }
     }
 #pragma unroll
@@ -293,8 +333,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
 }
 
 template <int D, int DG>
-void launch_prep_t(const PrepParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((prep_kernel<D, DG>), dim3(grid), dim3(256), 0, s, p);
+void launch_gate_t(const GateParams& p, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((gate_kernel<D, DG>), dim3(grid), dim3(kGateThreads), lds, s, p);
 }
 
 }  // namespace
@@ -303,10 +343,6 @@ float log_threshold(float tau);
 
 int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   PrepParams p{};
-  p.q_nope = a.q_nope;
-  p.w_q = a.w_q;
-  p.q_gate = a.q_gate;
-  p.n_query_wgs = a.q_gate ? d.num_kv_heads * (d.d_gate / 16) * ((d.batch + 15) / 16) : 0;
   p.k_nope = a.k_nope;
   p.w_k = a.w_k;
   p.kcomp_lens = a.kcomp_lens;
@@ -316,23 +352,17 @@ int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   p.sb = d.kv_stride_b;
   p.sh = d.kv_stride_h;
   p.st = d.kv_stride_t;
-  p.B = d.batch;
-  p.Hq = d.num_q_heads;
   p.Hkv = d.num_kv_heads;
-  p.G = d.num_q_heads / d.num_kv_heads;
   p.BS = d.block_size;
   p.Lmax = d.max_seq_len;
   p.NBmax = static_cast<int>(nb_max(&d));
   p.freqs = make_freqs(d.d_gate, a.theta);
-  const int64_t cache_wgs = (a.kcomp != nullptr && a.max_new_blocks > 0)
-                                ? static_cast<int64_t>(d.batch) * d.num_kv_heads * a.max_new_blocks
-                                : 0;
-  const int64_t grid = p.n_query_wgs + cache_wgs;
+  const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads * a.max_new_blocks;
   if (grid > 0x7fffffff) {
-    set_error("gate prep grid too large");
+    set_error("cache update grid too large");
     return SEER_ERR_UNSUPPORTED;
   }
-  if (grid == 0) return SEER_OK;
+  if (grid <= 0) return SEER_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int key = (d.head_dim == 128 ? 2 : 0) | (d.d_gate == 128 ? 1 : 0);
   switch (key) {
@@ -341,7 +371,7 @@ int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
     case 2: launch_prep_t<128, 64>(p, static_cast<int>(grid), s); break;
     default: launch_prep_t<128, 128>(p, static_cast<int>(grid), s); break;
   }
-  return check_launch("gate prep launch");
+  return check_launch("cache update launch");
 }
 
 int launch_commit(const seer_dims& d, const int32_t* seq_lens, int32_t* kcomp_lens, int max_new,
@@ -354,16 +384,29 @@ int launch_commit(const seer_dims& d, const int32_t* seq_lens, int32_t* kcomp_le
 }
 
 int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
+  if (a.max_new < 0 || a.max_new > kMaxInlineNew) {
+    set_error("gate launch: too many new cache entries for one launch");
+    return SEER_ERR_INVALID_ARG;
+  }
   GateParams p{};
-  p.q_gate = a.q_gate;
+  p.q_nope = a.q_nope;
+  p.w_q = a.w_q;
+  p.q_gate_out = a.q_gate;
+  p.k_nope = a.k_nope;
+  p.w_k = a.w_k;
+  p.sb = d.kv_stride_b;
+  p.sh = d.kv_stride_h;
+  p.st = d.kv_stride_t;
+  p.max_new = a.max_new;
   p.kcomp = a.kcomp;
   p.kcomp_lens = a.kcomp_lens;
   p.seq_lens = a.seq_lens;
   p.logits_out = a.logits_out;
   p.block_idx = a.block_idx;
   p.num_selected = a.num_selected;
-  p.pending_new = a.pending_new;
+  p.Hq = d.num_q_heads;
   p.Hkv = d.num_kv_heads;
+  p.G = d.num_q_heads / d.num_kv_heads;
   p.BS = d.block_size;
   p.Lmax = d.max_seq_len;
   p.NBmax = static_cast<int>(nb_max(&d));
@@ -372,6 +415,7 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   p.max_sel = a.max_selected;
   p.log_tau = log_threshold(a.tau);
   p.inv_sqrt_dg = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d_gate)));
+  p.freqs = make_freqs(d.d_gate, a.theta);
   const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads;
   if (grid > 0x7fffffff) {
     set_error("gate grid too large");
@@ -379,10 +423,13 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   }
   const size_t lds = static_cast<size_t>(p.NBmax) * sizeof(uint32_t);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d.d_gate == 128)
-    hipLaunchKernelGGL(gate_kernel<128>, dim3(grid), dim3(kGateThreads), lds, s, p);
-  else
-    hipLaunchKernelGGL(gate_kernel<64>, dim3(grid), dim3(kGateThreads), lds, s, p);
+  const int key = (d.head_dim == 128 ? 2 : 0) | (d.d_gate == 128 ? 1 : 0);
+  switch (key) {
+    case 0: launch_gate_t<64, 64>(p, static_cast<int>(grid), lds, s); break;
+    case 1: launch_gate_t<64, 128>(p, static_cast<int>(grid), lds, s); break;
+    case 2: launch_gate_t<128, 64>(p, static_cast<int>(grid), lds, s); break;
+    default: launch_gate_t<128, 128>(p, static_cast<int>(grid), lds, s); break;
+  }
   return check_launch("gate launch");
 }
 

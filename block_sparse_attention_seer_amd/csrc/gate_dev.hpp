@@ -65,15 +65,16 @@ struct CompressSmem {
 //   of tokens, then threads < D fold the groups in a fixed order;
 //   GEMV: wave w of the 256 handles rows w, w+4, ...; lanes split the 3d
 //   columns and reduce across the wave;
-//   RoPE at position j*b (float64 angle), bf16 store (round to nearest even).
+//   RoPE at position j*b (float64 angle), bf16 store (round to nearest even)
+//   to dst and, when lds_copy is not null, to LDS as well.
+//   wf is this thread's RoPE frequency, theta^(-2(t mod DG/2)/DG) for thread t.
 template <int D, int DG>
 __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* row 0 of block */,
-                               int64_t st, int BS, const uint16_t* w_k_h, const RopeFreqs& freqs,
-                               int j, uint16_t* dst) {
+                               int64_t st, int BS, const uint16_t* w_k_h, double wf, int j,
+                               uint16_t* dst, uint16_t* lds_copy = nullptr) {
   constexpr int CP = CompressSmem<D, DG>::CP;
   constexpr int NTG = CompressSmem<D, DG>::NTG;
   const int tid = threadIdx.x;
-  const double wf = freqs.w[tid % (DG / 2)];  // requested early, used by the rotation
   if (tid < 256) {
     const int cp = tid % CP;
     const int tg = tid / CP;
@@ -122,8 +123,13 @@ __device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* 
   if (tid < DG / 2) {
     float olo, ohi;
     rope_pair(static_cast<double>(j) * BS, wf, sm.v[tid], sm.v[tid + DG / 2], &olo, &ohi);
-    dst[tid] = f2bf(olo);
-    dst[tid + DG / 2] = f2bf(ohi);
+    const uint16_t lo = f2bf(olo), hi = f2bf(ohi);
+    dst[tid] = lo;
+    dst[tid + DG / 2] = hi;
+    if (lds_copy != nullptr) {
+      lds_copy[tid] = lo;
+      lds_copy[tid + DG / 2] = hi;
+    }
   }
 }
 

@@ -137,18 +137,12 @@ int seer_gate_scores(const seer_dims* dims, const uint16_t* q_nope, const uint16
   if (workspace == nullptr || workspace_bytes < seer::gate_workspace_bytes(dims))
     return fail(SEER_ERR_WORKSPACE, "gate workspace missing or smaller than seer_gate_workspace_bytes()");
   SEER_CHECK(check_ptr(workspace, 16, "workspace", &why_));
-  float* q_gate = static_cast<float*>(workspace);
-  seer::PrepArgs pa{};
-  pa.q_nope = q_nope;
-  pa.w_q = w_q;
-  pa.q_gate = q_gate;
-  pa.seq_lens = seq_lens;
-  pa.theta = rope_theta;
-  int rc = seer::launch_prep(*dims, pa, stream);
-  if (rc != SEER_OK) return rc;
   seer::GateArgs ga{};
-  ga.q_gate = q_gate;
-  ga.kcomp = kcomp;
+  ga.q_nope = q_nope;
+  ga.w_q = w_q;
+  ga.q_gate = static_cast<float*>(workspace);
+  ga.theta = rope_theta;
+  ga.kcomp = const_cast<uint16_t*>(kcomp);  // read only: no new entries in this launch
   ga.kcomp_lens = kcomp_lens;
   ga.seq_lens = seq_lens;
   ga.logits_out = logits;
@@ -296,29 +290,39 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
   if (max_new_blocks > seer::nb_max(dims)) max_new_blocks = static_cast<int32_t>(seer::nb_max(dims));
 
-  // Launch 1: gate-query tiles plus the entries of newly completed blocks.
-  // Launch 2: logits and selection per (b, h), counting those entries.
-  // Launch 3: the sparse decode, which also commits them to kcomp_lens.
-  float* q_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec_bytes);
-  seer::PrepArgs pa{};
-  pa.q_nope = q_nope;
-  pa.w_q = w_q;
-  pa.q_gate = q_gate;
-  pa.k_nope = k_nope;
-  pa.w_k = w_k;
-  pa.kcomp_lens = kcomp_lens;
-  pa.kcomp = max_new_blocks > 0 ? kcomp : nullptr;
-  pa.max_new_blocks = max_new_blocks;
-  pa.seq_lens = seq_lens;
-  pa.theta = rope_theta;
-  int rc = seer::launch_prep(*dims, pa, stream);
-  if (rc != SEER_OK) return rc;
+  // Launch 1: per (b, h), the entries of newly completed blocks, the gate
+  // query, the logits and the selection.  Launch 2: the sparse decode, which
+  // also raises kcomp_lens over those entries.  More new blocks than one
+  // gate launch computes (a catch-up after a prompt) take the staged update
+  // first.
+  int rc = SEER_OK;
+  int inline_new = max_new_blocks;
+  if (max_new_blocks > seer::kMaxInlineNew) {
+    seer::PrepArgs pa{};
+    pa.k_nope = k_nope;
+    pa.w_k = w_k;
+    pa.kcomp_lens = kcomp_lens;
+    pa.kcomp = kcomp;
+    pa.max_new_blocks = max_new_blocks;
+    pa.seq_lens = seq_lens;
+    pa.theta = rope_theta;
+    rc = seer::launch_prep(*dims, pa, stream);
+    if (rc != SEER_OK) return rc;
+    rc = seer::launch_commit(*dims, seq_lens, kcomp_lens, max_new_blocks, stream);
+    if (rc != SEER_OK) return rc;
+    inline_new = 0;
+  }
   seer::GateArgs ga{};
-  ga.q_gate = q_gate;
+  ga.q_nope = q_nope;
+  ga.w_q = w_q;
+  ga.q_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec_bytes);
+  ga.theta = rope_theta;
+  ga.k_nope = k_nope;
+  ga.w_k = w_k;
+  ga.max_new = inline_new;
   ga.kcomp = kcomp;
   ga.kcomp_lens = kcomp_lens;
   ga.seq_lens = seq_lens;
-  ga.pending_new = max_new_blocks;
   ga.logits_out = logits;
   ga.block_idx = block_idx;
   ga.num_selected = num_selected;
@@ -330,7 +334,7 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   if (rc != SEER_OK) return rc;
   return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,
                        scale, s, workspace, dec_bytes, out, lse, stream,
-                       max_new_blocks > 0 ? kcomp_lens : nullptr, max_new_blocks);
+                       inline_new > 0 ? kcomp_lens : nullptr, inline_new);
 }
 
 size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selected,

@@ -15,6 +15,7 @@ constexpr int kMaxGroup = 16;          // query heads per KV head (MFMA N = 16)
 constexpr int kMaxNBSelect = 8192;     // blocks per sequence the select kernel holds in LDS
 constexpr int kMaxSplit = 128;         // splits per (b, h) in the decode kernel
 constexpr int kDecodeMergeLds = 48 * 1024;  // LDS bytes for the decode wave merge
+constexpr int kMaxInlineNew = 4;       // new cache entries the gate launch computes itself
 constexpr int kCounterBytes = 256;     // alignment of the partial outputs after the partial lse
 
 // ------------------------------------------------------- argument checks
@@ -40,17 +41,14 @@ const char* last_error();
 
 // ------------------------------------------------------ kernel launchers
 // Implemented in the .hip files.  Arguments were validated by the caller.
-// One launch for the gate-query tiles (when q_gate != nullptr) and the
-// cache-entry tasks (entries kcomp_lens[b] + z, z < max_new_blocks, of every
-// (b, h) whose block is complete; when kcomp != nullptr).
+// The staged cache update: entries kcomp_lens[b] + z, z < max_new_blocks,
+// of every (b, h) whose block is complete; launch_commit then raises
+// kcomp_lens.
 struct PrepArgs {
-  const uint16_t* q_nope;
-  const uint16_t* w_q;
-  float* q_gate;  // [B, H_kv, d_gate] or nullptr
   const uint16_t* k_nope;
   const uint16_t* w_k;
   const int32_t* kcomp_lens;
-  uint16_t* kcomp;  // or nullptr
+  uint16_t* kcomp;
   int max_new_blocks;
   const int32_t* seq_lens;
   double theta;
@@ -59,14 +57,21 @@ int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream);
 int launch_commit(const seer_dims& d, const int32_t* seq_lens, int32_t* kcomp_lens, int max_new,
                   void* stream);
 
-// Per-(b, h) block logits from the gate query, and the selection when
-// block_idx != nullptr.
+// Per-(b, h) gate query and block logits, and the selection when block_idx
+// != nullptr.  With max_new > 0 (at most kMaxInlineNew) the launch first
+// computes the pair's entries kcomp_lens[b] .. +max_new-1 whose blocks are
+// complete and scores them too; kcomp_lens itself is not raised.
 struct GateArgs {
-  const float* q_gate;
-  const uint16_t* kcomp;
+  const uint16_t* q_nope;
+  const uint16_t* w_q;
+  float* q_gate;           // [B, H_kv, d_gate] copy of the gate queries, or nullptr
+  double theta;
+  const uint16_t* k_nope;  // needed when max_new > 0
+  const uint16_t* w_k;
+  int max_new;
+  uint16_t* kcomp;
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
-  int pending_new;         // entries appended this step and not yet counted
   float* logits_out;       // or nullptr
   int32_t* block_idx;      // selection when non-null
   int32_t* num_selected;
