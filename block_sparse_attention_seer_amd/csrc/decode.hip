@@ -43,6 +43,12 @@ namespace seer {
 namespace {
 
 constexpr int kIdxLds = 512;  // index-row entries staged in LDS per workgroup
+// 16-token tiles per chunk (2 or 4).  Measured on MI355X: 4 (32 KiB of K
+// and V in flight per wave at d = 128) streams faster than 2, whose finer
+// share per wave does not make up for the halved bytes in flight.
+constexpr int kTilesPerChunk = 4;
+constexpr int kMergeInline = 8;  // splits merged from registers in one round trip
+static_assert(kTilesPerChunk == 2 || kTilesPerChunk == 4, "tiles per chunk");
 
 struct DecodeParams {
   const uint16_t* q;
@@ -74,6 +80,7 @@ __device__ __forceinline__ uint32_t pick2(uint2 a, uint2 b, int j) {
 
 template <int D, int BS, bool DENSE, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
+  constexpr int TPC = kTilesPerChunk;  // 16-token tiles per chunk
   constexpr int KS = D / 32;   // k-steps of the score contraction
   constexpr int VH = D / 64;   // 64-dim halves of the value contraction
 
@@ -118,12 +125,12 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     nslots = p.num_selected[pair];
     nslots = min(max(nslots, 0), p.max_sel);
   }
-  // Work unit: a 64-token chunk (four 16-token tiles) of an active block.
+  // Work unit: a chunk of TPC 16-token tiles of an active block.
   // The pair's chunks are cut into S even ranges, one per split; wave w of a
   // split takes chunks c_begin + w, c_begin + w + NW, ...  (A fixed
   // assignment keeps the summation order, and so the output bits, the same
   // from run to run.)
-  constexpr int CPB = BS / 64;
+  constexpr int CPB = BS / (16 * TPC);  // chunks per block
   const int nchunks = nslots * CPB;
   const int c_begin = static_cast<int>(static_cast<int64_t>(nchunks) * split / S);
   const int c_end = static_cast<int>(static_cast<int64_t>(nchunks) * (split + 1) / S);
@@ -151,17 +158,17 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   for (int c = c_begin + w; c < c_end; c += NW) {
     const int slot = c / CPB;
     const int blk = DENSE ? slot : (slot < kIdxLds ? s_idx[slot] : idx[slot]);
-    const int base = blk * BS + (c - slot * CPB) * 64;
+    const int base = blk * BS + (c - slot * CPB) * (16 * TPC);
     if (blk < 0 || blk >= nblk || base >= L) continue;  // invalid entry: skipped
-    // first token of each of the four tiles, or -1 past the sequence
-    int tok0[4];
+    // first token of each of the chunk's tiles, or -1 past the sequence
+    int tok0[TPC];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) tok0[nt] = (base + 16 * nt < L) ? base + 16 * nt : -1;
+    for (int nt = 0; nt < TPC; ++nt) tok0[nt] = (base + 16 * nt < L) ? base + 16 * nt : -1;
 
     // K rows tok0 + ln, dims 32*s + 8*lq .. +7 (the A operand).
-    uint4 kr[4][KS];
+    uint4 kr[TPC][KS];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < TPC; ++nt) {
       if (tok0[nt] >= 0) {
         const int row = min(tok0[nt] + ln, last);
         const uint16_t* kp = kb + row * p.st + 8 * lq;
@@ -173,9 +180,9 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
       }
     }
     // V rows tok0 + 4*lq + r, dims 64*hh + 4*ln .. +3.
-    uint2 vr[4][4][VH];
+    uint2 vr[TPC][4][VH];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < TPC; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (tok0[nt] >= 0) {
@@ -193,9 +200,9 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
 
     // Scores: sc[nt][r] = S[token tok0[nt] + 4 lq + r][head ln].
-    f32x4_t sc[4];
+    f32x4_t sc[TPC];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < TPC; ++nt) {
       sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) sc[nt] = mfma16x16x32(kr[nt][s], qop[s], sc[nt]);
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 
     float mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < TPC; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tok0[nt] + 4 * lq + r;
@@ -220,10 +227,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 
     // Probabilities, rounded to bf16 once; the row sum uses the rounded
     // values so that O is an exact convex combination of the V rows.
-    uint32_t pk[4][2];
+    uint32_t pk[TPC][2];
     float psum = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < TPC; ++nt)
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const float p0 = fast_exp2(sc[nt][2 * rr] - m_new);
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     // O[head][64 hh + 4 ln + j] += P[head][tokens] . V[tokens][..]; the 8
     // tokens of k-group lq in step s2 are tok0[2 s2 + kk/4] + 4 lq + kk%4.
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < TPC / 2; ++s2) {
       const uint4 pa = make_uint4(pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]);
 #pragma unroll
       for (int hh = 0; hh < VH; ++hh)
@@ -339,34 +346,72 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   if (!sm_last) return;
   const float* plse = p.part_lse + static_cast<int64_t>(pair) * S * G;
   const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
-  for (int i = tid; i < S * G; i += NW * 64)
-    sm_w[i] = __hip_atomic_load(plse + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (tid < G) {
-    const int head = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, sm_w[s * G + head]);
-    float tot = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ls = sm_w[s * G + head];
-      const float f = (M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
-      sm_w[s * G + head] = f;
-      tot += f;
+  if (S <= kMergeInline) {
+    // one round trip: each element's S partial outputs and its head's S
+    // partial lse values are requested together; the weights are formed per
+    // element, in the same order as below
+    for (int e = tid; e < nel; e += NW * 64) {
+      const int head = e / D;
+      const int dim = e - head * D;
+      float ls[kMergeInline], os[kMergeInline];
+#pragma unroll
+      for (int s = 0; s < kMergeInline; ++s) {
+        if (s < S) {
+          ls[s] = __hip_atomic_load(plse + s * G + head, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          os[s] = __hip_atomic_load(po + (s * G + head) * D + dim, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < kMergeInline; ++s)
+        if (s < S) M = fmaxf(M, ls[s]);
+      float f[kMergeInline];
+      float tot = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMergeInline; ++s) {
+        f[s] = (s < S && M != -INFINITY && ls[s] != -INFINITY) ? fast_exp2(ls[s] - M) : 0.f;
+        tot += f[s];
+      }
+      const float inv = tot > 0.f ? 1.f / tot : 0.f;
+      float o = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMergeInline; ++s)
+        if (s < S) o += (f[s] * inv) * os[s];
+      p.out[(out_base + head) * D + dim] = f2bf(o);
+      if (dim == 0 && p.lse != nullptr)
+        p.lse[out_base + head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
     }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    for (int s = 0; s < S; ++s) sm_w[s * G + head] *= inv;
-    sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  for (int e = tid; e < nel; e += NW * 64) {
-    const int head = e / D;
-    const int dim = e - head * D;
-    float o = 0.f;
-    for (int s = 0; s < S; ++s)
-      o += sm_w[s * G + head] *
-           __hip_atomic_load(po + (s * G + head) * D + dim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    p.out[(out_base + head) * D + dim] = f2bf(o);
-    if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
+  } else {
+    for (int i = tid; i < S * G; i += NW * 64)
+      sm_w[i] = __hip_atomic_load(plse + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid < G) {
+      const int head = tid;
+      float M = -INFINITY;
+      for (int s = 0; s < S; ++s) M = fmaxf(M, sm_w[s * G + head]);
+      float tot = 0.f;
+      for (int s = 0; s < S; ++s) {
+        const float ls = sm_w[s * G + head];
+        const float f = (M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
+        sm_w[s * G + head] = f;
+        tot += f;
+      }
+      const float inv = tot > 0.f ? 1.f / tot : 0.f;
+      for (int s = 0; s < S; ++s) sm_w[s * G + head] *= inv;
+      sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    for (int e = tid; e < nel; e += NW * 64) {
+      const int head = e / D;
+      const int dim = e - head * D;
+      float o = 0.f;
+      for (int s = 0; s < S; ++s)
+        o += sm_w[s * G + head] * __hip_atomic_load(po + (s * G + head) * D + dim, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+      p.out[(out_base + head) * D + dim] = f2bf(o);
+      if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
+    }
   }
   if (tid == 0) __hip_atomic_store(p.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
