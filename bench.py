@@ -157,6 +157,21 @@ def main() -> int:
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # the same step replayed from HIP graphs (one per replica), for the
+    # launch overhead the eager loop above pays on the host
+    graphs = []
+    for inp, st in reps:
+        graphs.append(st.capture_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                                      inp["w_k"], inp["seq_lens"], scale, 1, False))
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / args.steps
+
     # the dominant kernel alone, event-timed on the stream it runs on, on the
     # same replicas and the selections the steps just made
     # (the binding launches on torch's current stream, which these events see)
@@ -259,6 +274,7 @@ def main() -> int:
                       "launches (same replicas and selections as the timed steps); avg = "
                       "elapsed / K",
         },
+        "step_us_graph_replay": round(graph_us, 3),
         "step_algorithmic_bytes": int(step_alg),
         "step_GBps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / PEAK_GBPS, 4),

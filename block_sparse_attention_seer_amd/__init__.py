@@ -387,6 +387,27 @@ class DecodeStep:
                            self.lse)
         return self.out, self.lse
 
+    def capture_step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                     scale: Optional[float] = None, max_new_blocks: int = 1,
+                     keep_logits: bool = False) -> "torch.cuda.CUDAGraph":
+        """Records one fused step on these buffers into a HIP graph.
+
+        ``graph.replay()`` then runs the step on the buffers' contents at
+        replay time (the caller updates them in place, e.g. appends a token
+        and bumps seq_lens), with no host work per step.  The step records
+        no memory sets and leaves its split counters at zero, so replays are
+        independent.  One eager step runs first (library set-up happens
+        outside the capture); it leaves the same state a replay would.
+        """
+        self.fused_step(q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens, scale,
+                        max_new_blocks, keep_logits)
+        torch.cuda.synchronize(self.device)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.fused_step(q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens, scale,
+                            max_new_blocks, keep_logits)
+        return graph
+
     def fused_step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
                    scale: Optional[float] = None, max_new_blocks: int = 1,
                    keep_logits: bool = True):

@@ -625,3 +625,45 @@ def test_pipeline_full_size_sampled(S):
             _check_pair(w, inp, st, b, h, f"pipeline full b={b} h={h} L={int(now[b])}")
     del inp
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- graph capture
+
+def test_graph_replays_equal_eager_steps(S):
+    """A captured fused step, replayed after eager appends (some of which
+    complete a block) with unrelated eager work in between, gives bit for bit
+    what the eager fused step gives on the same state, replay after replay."""
+    from workloads import append_token
+    w = WORKLOADS["pipeline_128k"].replace(batch=4, max_seq_len=4096, seq_len_range=(700, 900))
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    eager = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    graphed = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    eager.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    _clone_state(eager, graphed)
+    other = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+            inp["seq_lens"])
+    graph = graphed.capture_step(*args)
+    eager.fused_step(*args, keep_logits=False)
+    gen = torch.Generator(device=DEV).manual_seed(80)
+    completed = 0
+    for step in range(70):
+        before = inp["seq_lens"].clone()
+        append_token(inp, gen)
+        completed += int(((inp["seq_lens"] // 64) != (before // 64)).sum())
+        other.step(*args)  # eager work between replays
+        graph.replay()
+        eager.fused_step(*args, keep_logits=False)
+        if step % 10 == 9 or step == 69:
+            torch.cuda.synchronize()
+            say(f"graph replay {step}")
+            assert torch.equal(graphed.kcomp_lens, eager.kcomp_lens), step
+            assert torch.equal(graphed.kcomp, eager.kcomp), step
+            assert torch.equal(graphed.block_idx, eager.block_idx), step
+            assert torch.equal(graphed.num_selected, eager.num_selected), step
+            assert torch.equal(graphed.out, eager.out), step
+            assert torch.equal(graphed.lse, eager.lse), step
+    assert completed > 0  # some replays appended cache entries
+    _check_pair(w, inp, graphed, 0, 0, "graph replay vs oracle")
