@@ -53,6 +53,7 @@ __all__ = [
     "gate_logits",
     "select_topk",
     "select_threshold",
+    "select_topp",
     "blocks_to_tokens",
     "attention_gathered",
     "attention_masked_dense",
@@ -277,6 +278,37 @@ def select_threshold(z: np.ndarray, tau: float, seq_len: int, block_size: int,
     return out if capacity is None else out[:capacity]
 
 
+def select_topp(z: np.ndarray, p: float, seq_len: int, block_size: int,
+                capacity: Optional[int] = None) -> np.ndarray:
+    """Top-p (nucleus) selection: the smallest set of scored blocks, taken in
+    descending score order (equal scores: lower index first), whose softmax
+    probability mass reaches p; plus the forced blocks.
+
+    [CP Knowl 14] names top-p sparsity as the adaptive direction beyond the
+    fixed budget of [CP Knowl 5]; the set is read as the usual nucleus: walk
+    the blocks from the highest score and stop as soon as the mass taken so
+    far is at least p (p <= 0 takes none, a p the total never reaches takes
+    all).  The softmax runs over the scored blocks, in float64.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    n = z.shape[0]
+    chosen = []
+    if n > 0:
+        m = z.max()
+        e = np.exp(z - m)
+        prob = e / float(np.sum(e))
+        order = sorted(range(n), key=lambda j: (-z[j], j))
+        mass = 0.0
+        for j in order:
+            if mass >= p:
+                break
+            chosen.append(j)
+            mass += float(prob[j])
+    chosen += _forced_blocks(n, seq_len, block_size)
+    out = np.asarray(sorted(chosen), dtype=np.int64)
+    return out if capacity is None else out[:capacity]
+
+
 def topk_budget_blocks(token_budget: int, block_size: int) -> int:
     """[CP Knowl 5]: a token budget B becomes a block budget k = ceil(B/b)."""
     return -(-int(token_budget) // int(block_size))
@@ -371,6 +403,7 @@ def decode_pair(q_nope: np.ndarray, q: np.ndarray, k_nope: np.ndarray,
 
     q_nope, q: [g, d] (pre- and post-RoPE query heads of the group);
     k_nope, k, v: [>= seq_len, d]; kcomp: [n_cached, d_gate] cache entries.
+    tau is the threshold (mode "threshold") or the mass p (mode "topp").
     Returns dict(q_gate, logits, blocks, o, lse).
     """
     g, d = np.asarray(q).shape
@@ -382,6 +415,8 @@ def decode_pair(q_nope: np.ndarray, q: np.ndarray, k_nope: np.ndarray,
         blocks = select_topk(z, topk, seq_len, block_size, capacity)
     elif mode == "threshold":
         blocks = select_threshold(z, tau, seq_len, block_size, capacity)
+    elif mode == "topp":
+        blocks = select_topp(z, tau, seq_len, block_size, capacity)
     else:
         raise ValueError(mode)
     o, lse = sparse_decode_pair(q, k, v, seq_len, blocks, block_size, scale)

@@ -270,6 +270,51 @@ def test_threshold_is_strict():
     assert list(O.select_threshold(np.array([0.3, -1.0, 2.0]), 0.0, 3 * b, b)) == [0, 1, 2]
 
 
+def test_topp_matches_brute_force_smallest_set():
+    """[CP Knowl 14] top-p read as the nucleus: among all block sets whose
+    softmax mass reaches p, the smallest; among those the heaviest (unique for
+    distinct scores).  Brute force over all subsets of 10 blocks."""
+    import itertools
+    rng = np.random.default_rng(14)
+    b = 64
+    for trial in range(12):
+        n = 10
+        z = rng.normal(scale=1.5, size=n)
+        prob = scipy.special.softmax(z)
+        for pmass in [0.05, 0.3, 0.5, 0.77, 0.9, 0.99]:
+            best = None
+            for r in range(0, n + 1):
+                feas = [c for c in itertools.combinations(range(n), r)
+                        if prob[list(c)].sum() >= pmass]
+                if feas:
+                    best = max(feas, key=lambda c: prob[list(c)].sum())
+                    break
+            cum = np.sort(prob)[::-1].cumsum()
+            if np.min(np.abs(cum - pmass)) < 1e-12:
+                continue  # the boundary itself is a rounding question
+            assert list(O.select_topp(z, pmass, n * b, b)) == sorted(best), (trial, pmass)
+
+
+def test_topp_special_cases_ties_and_partial_block():
+    b = 64
+    z = np.array([1.0, 2.0, 2.0, 0.0])
+    p = scipy.special.softmax(z)
+    assert list(O.select_topp(z, 0.0, 4 * b, b)) == []                  # nothing needed
+    assert list(O.select_topp(z, 1e-12, 4 * b, b)) == [1]               # the top block, lower index
+    assert list(O.select_topp(z, p[1] + 1e-9, 4 * b, b)) == [1, 2]      # its tie comes next
+    assert list(O.select_topp(z, 1.0, 4 * b, b)) == [0, 1, 2, 3]        # all
+    assert list(O.select_topp(z, 2.0, 4 * b, b)) == [0, 1, 2, 3]        # unreachable: all
+    assert list(O.select_topp(z, 0.3, 4 * b + 7, b)) == [1, 4]          # partial block 4 forced
+    assert list(O.select_topp(z, 0.5, 4 * b + 7, b)) == [1, 2, 4]
+    assert list(O.select_topp(np.zeros(0), 0.9, 20, b)) == [0]          # L < b
+    # the top-p set is the top-k set for its own size (distinct scores)
+    rng = np.random.default_rng(15)
+    for trial in range(30):
+        zz = rng.normal(size=int(rng.integers(2, 40)))
+        sel = O.select_topp(zz, float(rng.uniform(0.1, 0.99)), len(zz) * b, b)
+        assert list(sel) == list(O.select_topk(zz, len(sel), len(zz) * b, b))
+
+
 @pytest.mark.parametrize("mode", ["topk", "threshold"])
 def test_partial_block_always_selected_even_if_disfavoured(mode):
     rng = np.random.default_rng(11)
