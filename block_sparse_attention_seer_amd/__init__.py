@@ -29,7 +29,7 @@ import torch
 
 __all__ = [
     "SeerError", "SeerDims", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
-    "SELECT_TOPK", "SELECT_THRESHOLD", "make_dims",
+    "SELECT_TOPK", "SELECT_THRESHOLD", "SELECT_TOPP", "make_dims",
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
     "seer_sparse_decode", "seer_dense_decode", "seer_decode_step_workspace_bytes",
@@ -43,6 +43,7 @@ LIB_PATH = os.path.join(_HERE, "libseer.so")
 SEER_OK = 0
 SELECT_TOPK = 1
 SELECT_THRESHOLD = 2
+SELECT_TOPP = 3  # threshold carries the mass p
 
 EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
@@ -338,7 +339,8 @@ class DecodeStep:
         self.threshold = float(threshold)
         nbm = dims.nb_max
         if max_selected is None:
-            max_selected = nbm if self.mode == SELECT_THRESHOLD else min(self.topk_blocks + 1, nbm)
+            max_selected = (nbm if self.mode in (SELECT_THRESHOLD, SELECT_TOPP)
+                            else min(self.topk_blocks + 1, nbm))
         self.max_selected = int(max_selected)
         self.rope_theta = float(rope_theta)
         self.device = torch.device(device)

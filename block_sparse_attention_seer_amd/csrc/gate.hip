@@ -117,6 +117,7 @@ struct GateParams {
   int Hq, Hkv, G, BS, Lmax, NBmax;
   int mode, topk, max_sel;
   float log_tau;
+  uint32_t mass_target;  // top-p: ceil(p * 2^30)
   float inv_sqrt_dg;
   RopeFreqs freqs;
 };
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   nc0 = min(min(max(nc0, 0), p.NBmax), L / p.BS);  // cached blocks
   const int nc = min(L / p.BS, nc0 + p.max_new);   // scored: with this launch's entries
   const int nnew = nc - nc0;
-  if (tid < 256) s_sel.hist[tid] = 0;
+  select_smem_init(s_sel);
   const double wf = p.freqs.w[tid % (DG / 2)];
 
   // ---- all loads first: W_q rows and the query heads (first chunk group),
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   if (p.block_idx == nullptr) return;
   __syncthreads();
   select_blocks_wg<kGateThreads>(s_keys, s_sel, nc, (L + p.BS - 1) / p.BS, p.mode, p.topk,
-                                 p.log_tau, p.max_sel,
+                                 p.log_tau, p.mass_target, p.max_sel,
                                  p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
                                  p.num_selected + pair);
 }
@@ -340,6 +341,7 @@ void launch_gate_t(const GateParams& p, int grid, size_t lds, hipStream_t s) {
 }  // namespace
 
 float log_threshold(float tau);
+uint32_t topp_mass_target(float p);
 
 int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   PrepParams p{};
@@ -414,6 +416,7 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   p.topk = a.topk;
   p.max_sel = a.max_selected;
   p.log_tau = log_threshold(a.tau);
+  p.mass_target = topp_mass_target(a.tau);
   p.inv_sqrt_dg = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d_gate)));
   p.freqs = make_freqs(d.d_gate, a.theta);
   const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads;

@@ -58,13 +58,14 @@ int check_select_args(const seer_dims* dims, int32_t mode, int32_t topk_blocks, 
     const int64_t need = std::min<int64_t>(static_cast<int64_t>(topk_blocks) + 1, nbm);
     if (max_selected < need)
       return fail(SEER_ERR_INVALID_ARG, "max_selected must be >= min(topk_blocks + 1, NBmax)");
-  } else if (mode == SEER_SELECT_THRESHOLD) {
+  } else if (mode == SEER_SELECT_THRESHOLD || mode == SEER_SELECT_TOPP) {
     if (!(threshold >= 0.0f && threshold <= 1.0f))
-      return fail(SEER_ERR_INVALID_ARG, "threshold must be in [0, 1]");
+      return fail(SEER_ERR_INVALID_ARG, "threshold (tau or p) must be in [0, 1]");
     if (max_selected < nbm)
-      return fail(SEER_ERR_INVALID_ARG, "threshold mode needs max_selected >= NBmax");
+      return fail(SEER_ERR_INVALID_ARG, "threshold and top-p modes need max_selected >= NBmax");
   } else {
-    return fail(SEER_ERR_INVALID_ARG, "mode must be SEER_SELECT_TOPK or SEER_SELECT_THRESHOLD");
+    return fail(SEER_ERR_INVALID_ARG,
+                "mode must be SEER_SELECT_TOPK, SEER_SELECT_THRESHOLD or SEER_SELECT_TOPP");
   }
   if (max_selected < 1 || max_selected > nbm)
     return fail(SEER_ERR_INVALID_ARG, "max_selected must be in [1, NBmax]");

@@ -2,7 +2,8 @@
 //
 // [CP Knowl 5] (chapterpal page "SeerAttention-R: Sparse Attention
 // Adaptation for Long Reasoning"): token-budget top-k on un-softmaxed logits
-// or threshold on the softmax; the incomplete last block is always selected.
+// or threshold on the softmax; [CP Knowl 14]: top-p (nucleus) mass; the
+// incomplete last block is always selected.
 // One 512-thread workgroup per (sequence, KV head) loads the row of logits
 // into LDS and runs the selection shared with the fused gate kernel (same
 // workgroup size), so the staged and the fused paths select identically.
@@ -24,7 +25,8 @@ struct SelectParams {
   int32_t* block_idx;
   int32_t* num_selected;
   int Hkv, BS, Lmax, NBmax, mode, topk, max_sel;
-  float log_tau;  // ln(tau), -inf for tau = 0
+  float log_tau;         // ln(tau), -inf for tau = 0
+  uint32_t mass_target;  // top-p: ceil(p * 2^30)
 };
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
@@ -39,10 +41,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   nc = min(min(max(nc, 0), p.NBmax), L / p.BS);
   const float* z = p.logits + static_cast<int64_t>(pair) * p.NBmax;
   for (int j = threadIdx.x; j < nc; j += kSelThreads) s_keys[j] = __float_as_uint(z[j]);
-  if (threadIdx.x < 256) s_sel.hist[threadIdx.x] = 0;
+  select_smem_init(s_sel);
   __syncthreads();
   select_blocks_wg<kSelThreads>(s_keys, s_sel, nc, total_blocks, p.mode, p.topk, p.log_tau,
-                                p.max_sel, p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
+                                p.mass_target, p.max_sel,
+                                p.block_idx + static_cast<int64_t>(pair) * p.max_sel,
                                 p.num_selected + pair);
 }
 
@@ -52,12 +55,17 @@ float log_threshold(float tau) {
   return tau > 0.f ? static_cast<float>(std::log(static_cast<double>(tau))) : -INFINITY;
 }
 
+uint32_t topp_mass_target(float p) {
+  const double t = std::ceil(static_cast<double>(p) * 1073741824.0);
+  return t <= 0.0 ? 0u : (t >= 2147483647.0 ? 2147483647u : static_cast<uint32_t>(t));
+}
+
 int launch_select(const seer_dims& d, const SelectArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nbm = static_cast<int>(nb_max(&d));
   SelectParams p{a.logits, a.kcomp_lens, a.seq_lens, a.block_idx, a.num_selected,
                  d.num_kv_heads, d.block_size, d.max_seq_len, nbm, a.mode, a.topk,
-                 a.max_selected, log_threshold(a.tau)};
+                 a.max_selected, log_threshold(a.tau), topp_mass_target(a.tau)};
   const size_t lds = static_cast<size_t>(nbm) * sizeof(uint32_t);
   hipLaunchKernelGGL(select_kernel, dim3(d.batch * d.num_kv_heads), dim3(kSelThreads), lds, s, p);
   const hipError_t e = hipGetLastError();

@@ -36,11 +36,24 @@ constexpr int kSelMaxWaves = 16;
 
 struct SelectSmem {
   int hist[256];
+  int hmass[256];  // top-p: per-bucket mass in units of 2^-30 of the total
   float fred[2][kSelMaxWaves];
   uint32_t ured[2][kSelMaxWaves];
   int scan[2][kSelMaxWaves];
-  int pick[3];
+  int pick[4];
 };
+
+// Clears the histograms; call with every thread, then a barrier, before the
+// first selection.
+__device__ __forceinline__ void select_smem_init(SelectSmem& sm) {
+  if (threadIdx.x < 256) {
+    sm.hist[threadIdx.x] = 0;
+    sm.hmass[threadIdx.x] = 0;
+  }
+}
+
+// Top-p mass unit: 2^30 units make the whole softmax.
+constexpr float kMassUnits = 1073741824.f;
 
 // Makes the LDS writes of the NT selecting threads visible to all of them:
 // a workgroup barrier, or for a single wave only an ordering point (the LDS
@@ -162,6 +175,51 @@ __device__ __forceinline__ void hist_pick(SelectSmem& sm, int need, int& bucket,
   count = sm.pick[2];
 }
 
+// Top-p: after the mass histogram of this pass is complete (sm.hmass, with
+// the counts in sm.hist): the bucket where the mass accumulated from the top
+// first reaches `need`, the mass of the higher buckets, and the bucket's mass
+// and count.  Wave 0 scans and clears both histograms.  1 <= need <= counted
+// mass.
+template <int NT>
+__device__ __forceinline__ void hist_pick_mass(SelectSmem& sm, int need, int& bucket, int& above,
+                                               int& mass, int& count) {
+  sel_sync<NT>();
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    int hm[4], hc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hm[i] = sm.hmass[4 * lane + i];
+      hc[i] = sm.hist[4 * lane + i];
+      sm.hmass[4 * lane + i] = 0;
+      sm.hist[4 * lane + i] = 0;
+    }
+    const int mine = (hm[0] + hm[1]) + (hm[2] + hm[3]);
+    const int incl = wave_inclusive_scan(mine);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int suf = total - incl + mine;  // mass in buckets >= 4*lane
+    int cm = suf - mine;                  // mass in buckets >= 4*lane + 4
+    if (cm < need && need <= suf) {       // exactly one lane
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (cm + hm[i] >= need) {
+          sm.pick[0] = 4 * lane + i;
+          sm.pick[1] = cm;
+          sm.pick[2] = hm[i];
+          sm.pick[3] = hc[i];
+          break;
+        }
+        cm += hm[i];
+      }
+    }
+  }
+  sel_sync<NT>();
+  bucket = sm.pick[0];
+  above = sm.pick[1];
+  mass = sm.pick[2];
+  count = sm.pick[3];
+}
+
 // The keys j0 .. j0+n-1 of one thread: held in registers when KPL > 0 (n <=
 // KPL), else read from LDS on every visit.  each(f) calls f(j, z) in index
 // order.
@@ -194,7 +252,8 @@ struct KeyRange {
 template <int NT, int KPL>
 __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectSmem& sm, int nc,
                                                    int total_blocks, int mode, int topk,
-                                                   float log_tau, int max_sel, int32_t* out,
+                                                   float log_tau, uint32_t mass_target,
+                                                   int max_sel, int32_t* out,
                                                    int32_t* count_out) {
   static_assert(NT % 64 == 0 && NT / 64 <= kSelMaxWaves, "workgroup size");
   constexpr int NW = NT / 64;
@@ -274,6 +333,110 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
       }
       whole = (m == need);
     }
+  } else if (mode == SEER_SELECT_TOPP) {
+    // Top-p: the smallest prefix of the descending order whose softmax mass
+    // reaches p.  Each key's mass is w = rint(exp(z - max) / sum * 2^30)
+    // (sum in a fixed order; equal logits get equal w); the prefix ends at
+    // the first key where the running mass reaches T = ceil(p * 2^30).
+    // The narrowing is the top-k one with mass in place of counts; on a run
+    // of equal logits the first ceil(remaining / w) in index order are taken.
+    float mx = -INFINITY;
+    kr.each([&](int, float z) { mx = fmaxf(mx, z); });
+    mx = wave_max(mx);
+    if constexpr (NW > 1) {
+      if ((tid & 63) == 0) sm.fred[0][tid >> 6] = mx;
+      __syncthreads();
+      mx = sm.fred[0][0];
+#pragma unroll
+      for (int i = 1; i < NW; ++i) mx = fmaxf(mx, sm.fred[0][i]);
+    }
+    float se = 0.f;
+    kr.each([&](int, float z) { se += expf(z - mx); });
+    se = wave_sum(se);
+    if constexpr (NW > 1) {
+      if ((tid & 63) == 0) sm.fred[1][tid >> 6] = se;
+      __syncthreads();
+      se = sm.fred[1][0];
+#pragma unroll
+      for (int i = 1; i < NW; ++i) se += sm.fred[1][i];
+    }
+    const float unit = kMassUnits / se;
+    auto wmass = [&](float z) -> int { return static_cast<int>(rintf(expf(z - mx) * unit)); };
+    int wsum = 0;
+    kr.each([&](int, float z) { wsum += wmass(z); });
+    int total_mass;
+    (void)wg_exclusive_scan<NT>(wsum, sm.scan[0], &total_mass);
+    const int target = static_cast<int>(mass_target);
+    if (nc <= 0 || target <= 0) {
+      none = true;
+    } else if (target > total_mass) {
+      all = true;
+    } else {
+      int need_m = target;
+      int bmass = total_mass, bcount = nc;  // the kept bucket
+      float zmn = INFINITY, zmx = -INFINITY;
+      kr.each([&](int, float z) {
+        zmn = fminf(zmn, z);
+        zmx = fmaxf(zmx, z);
+      });
+      wg_minmax_f<NT>(zmn, zmx, sm);
+      const float scale = 256.f / (zmx - zmn);
+      uint32_t hi;
+      uint32_t kmn = 0xffffffffu, kmx = 0u;
+      if (zmx > zmn && scale > 0.f && scale < INFINITY) {
+        auto fbucket = [&](float z) -> int {
+          return (z == z) ? min(255, static_cast<int>((z - zmn) * scale)) : 0;
+        };
+        kr.each([&](int, float z) {
+          const int bkt = fbucket(z);
+          atomicAdd(&sm.hist[bkt], 1);
+          atomicAdd(&sm.hmass[bkt], wmass(z));
+        });
+        int b, above;
+        hist_pick_mass<NT>(sm, need_m, b, above, bmass, bcount);
+        need_m -= above;
+        kr.each([&](int, float z) {
+          if (fbucket(z) == b) {
+            const uint32_t key = float_key(z);
+            kmn = min(kmn, key);
+            kmx = max(kmx, key);
+          }
+        });
+      } else {
+        kr.each([&](int, float z) {
+          const uint32_t key = float_key(z);
+          kmn = min(kmn, key);
+          kmx = max(kmx, key);
+        });
+      }
+      wg_minmax_u<NT>(kmn, kmx, sm);
+      lo = kmn;
+      hi = kmx;
+      // narrow until the kept bucket is taken whole (its mass is exactly what
+      // is still needed, or it holds one key) or holds a single value
+      while (need_m < bmass && bcount > 1 && lo != hi) {
+        const int shift = max(0, 32 - __clz(static_cast<int>(hi - lo)) - 8);
+        kr.each([&](int, float z) {
+          const uint32_t key = float_key(z);
+          if (key >= lo && key <= hi) {
+            atomicAdd(&sm.hist[(key - lo) >> shift], 1);
+            atomicAdd(&sm.hmass[(key - lo) >> shift], wmass(z));
+          }
+        });
+        int b, above;
+        hist_pick_mass<NT>(sm, need_m, b, above, bmass, bcount);
+        need_m -= above;
+        const uint64_t nlo = static_cast<uint64_t>(lo) + (static_cast<uint64_t>(b) << shift);
+        const uint64_t nhi = nlo + (uint64_t{1} << shift) - 1;
+        lo = static_cast<uint32_t>(nlo);
+        hi = static_cast<uint32_t>(min(nhi, static_cast<uint64_t>(hi)));
+      }
+      whole = (need_m >= bmass || bcount == 1);
+      if (!whole) {  // bcount equal logits of mass bmass / bcount each
+        const int w0 = bmass / bcount;
+        need = (need_m + w0 - 1) / w0;
+      }
+    }
   } else {
     // softmax_j > tau  <=>  z_j > ln(tau) + logsumexp(z); fixed summation order
     float mx = -INFINITY;
@@ -299,7 +462,8 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
     thr = (nc > 0) ? log_tau + (mx + logf(se)) : INFINITY;
   }
 
-  const bool topk_range = (mode == SEER_SELECT_TOPK) && !all && !none;
+  const bool ranked = (mode == SEER_SELECT_TOPK || mode == SEER_SELECT_TOPP);
+  const bool topk_range = ranked && !all && !none;
   // ranks among the duplicates of lo, in index order (only if not whole)
   int eq_before = 0;
   if (topk_range && !whole) {
@@ -309,7 +473,7 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
     eq_before = wg_exclusive_scan<NT>(eq, sm.scan[0], &unused);
   }
   auto taken = [&](float z, int& rank) -> bool {
-    if (mode != SEER_SELECT_TOPK) return z > thr;
+    if (!ranked) return z > thr;
     if (all) return true;
     if (none) return false;
     const uint32_t key = float_key(z);
@@ -347,28 +511,29 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
 }
 
 // Called by all NT threads once keys[0..nc) (LDS, the logits as float bits)
-// are visible to every one of them.  sm.hist must be zero on entry and is
-// left zero.  Appends the unscored blocks nc .. total_blocks-1 and writes the
+// are visible to every one of them.  The histograms (select_smem_init) must
+// be zero on entry and are left zero.  mass_target = ceil(p * 2^30) for
+// top-p.  Appends the unscored blocks nc .. total_blocks-1 and writes the
 // ascending, -1 padded row out[0..max_sel) plus its count.  Up to 32 keys
 // per thread are held in registers.
 template <int NT>
 __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSmem& sm, int nc,
                                                  int total_blocks, int mode, int topk,
-                                                 float log_tau, int max_sel, int32_t* out,
-                                                 int32_t* count_out) {
+                                                 float log_tau, uint32_t mass_target,
+                                                 int max_sel, int32_t* out, int32_t* count_out) {
   const int vpt = (nc + NT - 1) / NT;
   if (vpt <= 1)
-    select_blocks_impl<NT, 1>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
-                              count_out);
+    select_blocks_impl<NT, 1>(keys, sm, nc, total_blocks, mode, topk, log_tau, mass_target,
+                              max_sel, out, count_out);
   else if (vpt <= 8)
-    select_blocks_impl<NT, 8>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
-                              count_out);
+    select_blocks_impl<NT, 8>(keys, sm, nc, total_blocks, mode, topk, log_tau, mass_target,
+                              max_sel, out, count_out);
   else if (vpt <= 32)
-    select_blocks_impl<NT, 32>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
-                               count_out);
+    select_blocks_impl<NT, 32>(keys, sm, nc, total_blocks, mode, topk, log_tau, mass_target,
+                               max_sel, out, count_out);
   else
-    select_blocks_impl<NT, 0>(keys, sm, nc, total_blocks, mode, topk, log_tau, max_sel, out,
-                              count_out);
+    select_blocks_impl<NT, 0>(keys, sm, nc, total_blocks, mode, topk, log_tau, mass_target,
+                              max_sel, out, count_out);
 }
 
 }  // namespace seer

@@ -74,7 +74,7 @@ enum {
   SEER_ERR_HIP = 4          /* HIP runtime error (launch, device query)     */
 };
 
-enum { SEER_SELECT_TOPK = 1, SEER_SELECT_THRESHOLD = 2 };
+enum { SEER_SELECT_TOPK = 1, SEER_SELECT_THRESHOLD = 2, SEER_SELECT_TOPP = 3 };
 
 typedef struct seer_dims {
   int32_t batch;        /* B >= 1                                           */
@@ -160,15 +160,24 @@ int seer_gate_scores(const seer_dims* dims, const uint16_t* q_nope,
  *              index.
  *   THRESHOLD: the j < n_c with logits[j] > ln(tau) + logsumexp(logits[0..n_c))
  *              (softmax_j > tau, strict), evaluated in float32.
+ *   TOPP:      the shortest run of the blocks in descending logit order
+ *              (equal logits: lower index first) whose softmax mass reaches
+ *              p ([CP Knowl 14] names top-p as the adaptive-sparsity
+ *              direction).  Each block's mass is rounded to a multiple of
+ *              2^-30 (float32 softmax); the run ends at the first block where
+ *              the running mass reaches ceil(p * 2^30) units.  p = 0 selects
+ *              no scored block; a p the total does not reach selects all.
  * plus every block in [n_c, N) (normally only the partial block).  Indices
  * are written ascending, -1 after the last; num_selected gets the count.
  * If more than max_selected blocks qualify (only when the cache lags), the
  * lowest max_selected are kept.
  *
- *   mode            SEER_SELECT_TOPK (uses topk_blocks >= 0) or
- *                   SEER_SELECT_THRESHOLD (uses 0 <= threshold <= 1).
+ *   mode            SEER_SELECT_TOPK (uses topk_blocks >= 0),
+ *                   SEER_SELECT_THRESHOLD (uses 0 <= threshold <= 1) or
+ *                   SEER_SELECT_TOPP (threshold is the mass p, 0..1).
  *   max_selected    capacity per (b, h): TOPK needs
- *                   >= min(topk_blocks + 1, NBmax), THRESHOLD needs >= NBmax.
+ *                   >= min(topk_blocks + 1, NBmax), THRESHOLD and TOPP need
+ *                   >= NBmax.
  *   NBmax <= 8192 (SEER_ERR_UNSUPPORTED otherwise).
  */
 int seer_select_blocks(const seer_dims* dims, const float* logits,

@@ -11,6 +11,9 @@ oracle on the same inputs):
     given the same cache;
   * top-k indices on identical float32 logits: exact;
   * threshold indices: exact wherever |z_j - (ln tau + LSE)| > 1e-3;
+  * top-p indices: a top prefix (ties to the lower index) that reaches p,
+    exact wherever the cumulative softmax mass at the cut is farther than
+    a margin (1e-5 on identical logits, 1e-3 end to end) from p;
   * end-to-end top-k: exact wherever the oracle's k-th / (k+1)-th logit gap
     exceeds 1e-3, otherwise the GPU's set must still be a valid top-k within
     1e-3.
@@ -110,3 +113,30 @@ def check_topk_set(gpu_blocks, ref_blocks, z_ref: np.ndarray, k: int, n_scored: 
 def threshold_value(z: np.ndarray, tau: float) -> float:
     m = z.max()
     return math.log(tau) + m + math.log(float(np.sum(np.exp(z - m))))
+
+
+def check_topp_set(got, z, p, nc, forced, what, eps):
+    """A top-p selection `got` (ascending, forced blocks included) against the
+    definition on logits z[:nc] (float64): its scored part must be the first s
+    blocks of the descending order (equal logits: lower index first), with
+    mass(first s) >= p - eps and mass(first s-1) < p + eps.  Returns whether
+    it equals the oracle's set exactly."""
+    z = np.asarray(z, dtype=np.float64)[:nc]
+    scored = [j for j in got if j < nc]
+    assert [j for j in got if j >= nc] == list(forced), f"{what}: forced blocks"
+    ref = O.select_topp(z, p, nc * 64 + 1, 64).tolist()  # scored part only
+    ref = [j for j in ref if j < nc]
+    if scored == ref:
+        return True
+    order = sorted(range(nc), key=lambda j: (-z[j], j))
+    s = len(scored)
+    assert sorted(scored) == sorted(order[:s]), f"{what}: not a top prefix"
+    if nc == 0:
+        return True
+    e = np.exp(z - z.max())
+    prob = e / e.sum()
+    cum = np.concatenate([[0.0], np.cumsum(prob[order])])
+    reach = cum[s] >= p - eps or s == nc
+    short_before = s == 0 or cum[s - 1] < p + eps
+    assert reach and short_before, f"{what}: top-p cut at {s} (mass {cum[s]:.9f}, p {p})"
+    return False

@@ -16,13 +16,14 @@ import pytest
 import torch
 
 import oracle as O
-from seer_testlib import (assert_lse_close, assert_out_close, bf16_ulp, check_topk_set, f64,
-                          host_inputs, oracle_chain, threshold_value)
+from seer_testlib import (assert_lse_close, assert_out_close, bf16_ulp, check_topk_set,
+                          check_topp_set, f64, host_inputs, oracle_chain, threshold_value)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+MODES = {"topk": 1, "threshold": 2, "topp": 3}  # the library's SEER_SELECT_* values
 
 
 def say(msg: str) -> None:
@@ -374,12 +375,43 @@ def test_select_threshold(S, nbm, bs, tau):
             assert np.all(idx[b, h, ns[b, h]:] == -1)
 
 
+@pytest.mark.parametrize("nbm,bs,pmass,quant", [(512, 64, 0.5, None), (512, 64, 0.9, None),
+                                               (64, 128, 0.999, None), (2048, 64, 0.3, None),
+                                               (300, 64, 0.7, 0.5), (100, 64, 0.0, None),
+                                               (100, 64, 1.0, None), (8192, 64, 0.95, None)])
+def test_select_topp(S, nbm, bs, pmass, quant):
+    say(f"select topp nbm={nbm} p={pmass} quant={quant}")
+    B, Hkv = 4, 3
+    lmax = nbm * bs
+    rng = np.random.default_rng(nbm + int(pmass * 100))
+    z = rng.normal(scale=2.0, size=(B, Hkv, nbm)).astype(np.float32)
+    if quant:  # many exact ties
+        z = (np.round(z / quant) * quant).astype(np.float32)
+    z[1, 0, 5] = -np.inf
+    z[1, 1, :] = 0.25  # all equal
+    z[2, 2, 3] = 30.0  # one block holds nearly all mass
+    seq = [lmax - 1, lmax, 5 * bs + 3, bs // 2]
+    kl = [s_ // bs for s_ in seq]
+    dims = S.make_dims(B, 4 * Hkv, Hkv, 128, 128, bs, lmax)
+    idx, ns = _run_select(S, dims, z, kl, seq, S.SELECT_TOPP, 0, pmass, nbm)
+    exact = 0
+    for b in range(B):
+        nc = seq[b] // bs
+        forced = list(range(nc, -(-seq[b] // bs)))
+        for h in range(Hkv):
+            got = idx[b, h, :ns[b, h]].tolist()
+            exact += check_topp_set(got, z[b, h].astype(np.float64), pmass, nc, forced,
+                                    f"b={b} h={h}", 1e-5)
+            assert np.all(idx[b, h, ns[b, h]:] == -1)
+    assert exact >= B * Hkv - 2
+
+
 # ----------------------------------------------------------- end to end
 
 def _run_workload_step(S, w, inp, num_split=0):
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, inp["k"].shape[2])
-    mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
+    mode = MODES[w.mode]
     st = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau,
                       num_split=num_split, device=DEV)
     seq = inp["seq_lens"]
@@ -401,6 +433,8 @@ def _check_pair(w, inp, st, b, h, what):
     forced = list(range(nc, -(-L // w.block_size)))
     if w.mode == "topk":
         same = check_topk_set(got, ref["blocks"], ref["logits"], w.topk_blocks, nc, forced, what)
+    elif w.mode == "topp":
+        same = check_topp_set(got, ref["logits"], w.tau, nc, forced, what, 1e-3)
     else:
         same = got == ref["blocks"].tolist()
         if not same:
@@ -498,6 +532,8 @@ def _clone_state(st_from, st_to):
     ("qwen3_8b_layer", {}),
     ("qwen3_14b_b16", dict(batch=4)),
     ("threshold_b128", dict(batch=6, max_seq_len=20000, seq_len_range=(3000, 20000))),
+    ("qwen3_14b_b16", dict(batch=3, mode="topp", tau=0.6)),
+    ("tiny", dict(seq_len=1000, mode="topp", tau=0.8)),
 ])
 def test_fused_step_equals_staged(S, name, overrides):
     """seer_decode_step reproduces the four staged calls bit for bit."""
@@ -506,10 +542,11 @@ def test_fused_step_equals_staged(S, name, overrides):
     inp = make_inputs(w, device=DEV)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
-    mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
+    mode = MODES[w.mode]
     a = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
     b = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
     c = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
+    assert a.mode == MODES[w.mode]
     seq = inp["seq_lens"]
     a.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
     _clone_state(a, b)
