@@ -11,7 +11,8 @@
 // Kernels:
 //   prep_kernel    cache-entry tasks of the staged update: one newly
 //                  completed block of one (sequence, KV head) each (pool,
-//                  W_k GEMV, RoPE, bf16).
+//                  W_k GEMV, RoPE, bf16); prep_bulk_kernel does eight
+//                  consecutive blocks per workgroup for large updates.
 //   commit_kernel  raises kcomp_lens once every new entry is written.
 //   gate_kernel    one 512-thread workgroup per (sequence, KV head): the
 //                  pair's new cache entries (fused step), its gate query
@@ -80,6 +81,35 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
                         dst);
 }
 
+// Bulk variant (a prompt's cache, or any update of many blocks): one
+// workgroup per kBulkBlocks consecutive new entries of one pair, so each W_k
+// row is read once for all of them.  The entries are bit-identical to the
+// one-block kernel's.
+constexpr int kBulkBlocks = 8;
+
+template <int D, int DG>
+__global__ __launch_bounds__(256) void prep_bulk_kernel(PrepParams p) {
+  __shared__ CompressSmem<D, DG, kBulkBlocks> cm;
+  const int per_pair = (p.max_new + kBulkBlocks - 1) / kBulkBlocks;
+  const int pair = blockIdx.x / per_pair;
+  const int z0 = (blockIdx.x - pair * per_pair) * kBulkBlocks;
+  const int b = pair / p.Hkv;
+  const int h = pair - b * p.Hkv;
+  int L = p.seq_lens[b];
+  L = min(max(L, 0), p.Lmax);
+  int cl = p.kcomp_lens[b];
+  cl = min(max(cl, 0), p.NBmax);
+  const int j0 = cl + z0;
+  const int nblk = min(kBulkBlocks, min(L / p.BS, cl + p.max_new) - j0);
+  if (nblk <= 0) return;  // uniform over the workgroup
+  const double wf = p.freqs.w[threadIdx.x % (DG / 2)];
+  const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j0) * p.BS * p.st;
+  uint16_t* dst = p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j0) * DG;
+  compress_blocks<D, DG, kBulkBlocks>(cm, keys, p.st, p.BS,
+                                      p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf, j0, nblk,
+                                      dst);
+}
+
 __global__ void commit_kernel(const int32_t* seq_lens, int32_t* kcomp_lens, int B, int BS, int Lmax,
                               int NBmax, int max_new) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -88,8 +118,11 @@ __global__ void commit_kernel(const int32_t* seq_lens, int32_t* kcomp_lens, int 
 }
 
 template <int D, int DG>
-void launch_prep_t(const PrepParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((prep_kernel<D, DG>), dim3(grid), dim3(256), 0, s, p);
+void launch_prep_t(const PrepParams& p, int grid, bool bulk, hipStream_t s) {
+  if (bulk)
+    hipLaunchKernelGGL((prep_bulk_kernel<D, DG>), dim3(grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((prep_kernel<D, DG>), dim3(grid), dim3(256), 0, s, p);
 }
 
 // ------------------------------------------------------------------ gate
@@ -359,7 +392,10 @@ int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   p.Lmax = d.max_seq_len;
   p.NBmax = static_cast<int>(nb_max(&d));
   p.freqs = make_freqs(d.d_gate, a.theta);
-  const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads * a.max_new_blocks;
+  const bool bulk = a.max_new_blocks >= kBulkBlocks;
+  const int64_t per_pair = bulk ? (a.max_new_blocks + kBulkBlocks - 1) / kBulkBlocks
+                                : a.max_new_blocks;
+  const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads * per_pair;
   if (grid > 0x7fffffff) {
     set_error("cache update grid too large");
     return SEER_ERR_UNSUPPORTED;
@@ -368,10 +404,10 @@ int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int key = (d.head_dim == 128 ? 2 : 0) | (d.d_gate == 128 ? 1 : 0);
   switch (key) {
-    case 0: launch_prep_t<64, 64>(p, static_cast<int>(grid), s); break;
-    case 1: launch_prep_t<64, 128>(p, static_cast<int>(grid), s); break;
-    case 2: launch_prep_t<128, 64>(p, static_cast<int>(grid), s); break;
-    default: launch_prep_t<128, 128>(p, static_cast<int>(grid), s); break;
+    case 0: launch_prep_t<64, 64>(p, static_cast<int>(grid), bulk, s); break;
+    case 1: launch_prep_t<64, 128>(p, static_cast<int>(grid), bulk, s); break;
+    case 2: launch_prep_t<128, 64>(p, static_cast<int>(grid), bulk, s); break;
+    default: launch_prep_t<128, 128>(p, static_cast<int>(grid), bulk, s); break;
   }
   return check_launch("cache update launch");
 }

@@ -48,89 +48,133 @@ __device__ __forceinline__ void rope_pair(double pos, double w, float lo, float 
   *out_hi = fmaf(hi, cs, lo * sn);
 }
 
-// Shared-memory scratch of one cache-entry computation.
-template <int D, int DG>
+// Shared-memory scratch of the cache-entry computation of up to NB blocks.
+template <int D, int DG, int NB = 1>
 struct CompressSmem {
   static constexpr int CP = D / 2;      // channel pairs
   static constexpr int NTG = 256 / CP;  // token groups
   float red[3][NTG][D];
-  float u[3 * D];
-  float v[DG];
+  float u[NB][3 * D];
+  float v[NB][DG];
 };
 
-// One K Compression Cache entry (block j of pair (b, h)) computed by the
-// first 256 threads of the workgroup; the caller provides the barrier
-// discipline (every thread of the workgroup must call this).
-//   pooling: each (channel pair, token group) thread reduces a strided set
-//   of tokens, then threads < D fold the groups in a fixed order;
-//   GEMV: wave w of the 256 handles rows w, w+4, ...; lanes split the 3d
-//   columns and reduce across the wave;
+// K Compression Cache entries of blocks j0 .. j0+nblk-1 (nblk <= NB,
+// consecutive blocks of one pair; keys points at row 0 of block j0, dst at
+// entry j0) computed by the first 256 threads of the workgroup; every thread
+// of the workgroup must call this (it contains barriers).  Each block's
+// arithmetic is the same for every NB and nblk, so an entry has the same bits
+// whichever way the cache is built.
+//   pooling, block by block: each (channel pair, token group) thread reduces
+//   a strided set of tokens, then threads < D fold the groups in a fixed
+//   order;
+//   GEMV: wave w of the 256 handles rows w, w+4, ... (loaded 8 rows at a
+//   time, each row applied to every block); lanes split the 3d columns and
+//   reduce across the wave;
 //   RoPE at position j*b (float64 angle), bf16 store (round to nearest even)
-//   to dst and, when lds_copy is not null, to LDS as well.
+//   to dst and, when lds_copy is not null, to LDS ([NB][DG]) as well.
 //   wf is this thread's RoPE frequency, theta^(-2(t mod DG/2)/DG) for thread t.
-template <int D, int DG>
-__device__ void compress_block(CompressSmem<D, DG>& sm, const uint16_t* keys /* row 0 of block */,
-                               int64_t st, int BS, const uint16_t* w_k_h, double wf, int j,
-                               uint16_t* dst, uint16_t* lds_copy = nullptr) {
-  constexpr int CP = CompressSmem<D, DG>::CP;
-  constexpr int NTG = CompressSmem<D, DG>::NTG;
+template <int D, int DG, int NB>
+__device__ void compress_blocks(CompressSmem<D, DG, NB>& sm, const uint16_t* keys, int64_t st,
+                                int BS, const uint16_t* w_k_h, double wf, int j0, int nblk,
+                                uint16_t* dst, uint16_t* lds_copy = nullptr) {
+  constexpr int CP = CompressSmem<D, DG, NB>::CP;
+  constexpr int NTG = CompressSmem<D, DG, NB>::NTG;
   const int tid = threadIdx.x;
-  if (tid < 256) {
-    const int cp = tid % CP;
-    const int tg = tid / CP;
-    const uint16_t* base = keys + 2 * cp;
-    float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY, s0 = 0.f, s1 = 0.f;
-    for (int t = tg; t < BS; t += NTG) {
-      const uint32_t wv = *reinterpret_cast<const uint32_t*>(base + t * st);
-      const float a = bf_lo(wv), bb = bf_hi(wv);
-      mx0 = fmaxf(mx0, a); mn0 = fminf(mn0, a); s0 += a;
-      mx1 = fmaxf(mx1, bb); mn1 = fminf(mn1, bb); s1 += bb;
+  for (int n = 0; n < nblk; ++n) {
+    if (tid < 256) {
+      const int cp = tid % CP;
+      const int tg = tid / CP;
+      const uint16_t* base = keys + static_cast<int64_t>(n) * BS * st + 2 * cp;
+      float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY, s0 = 0.f, s1 = 0.f;
+      for (int t = tg; t < BS; t += NTG) {
+        const uint32_t wv = *reinterpret_cast<const uint32_t*>(base + t * st);
+        const float a = bf_lo(wv), bb = bf_hi(wv);
+        mx0 = fmaxf(mx0, a); mn0 = fminf(mn0, a); s0 += a;
+        mx1 = fmaxf(mx1, bb); mn1 = fminf(mn1, bb); s1 += bb;
+      }
+      sm.red[0][tg][2 * cp] = mx0; sm.red[0][tg][2 * cp + 1] = mx1;
+      sm.red[1][tg][2 * cp] = mn0; sm.red[1][tg][2 * cp + 1] = mn1;
+      sm.red[2][tg][2 * cp] = s0;  sm.red[2][tg][2 * cp + 1] = s1;
     }
-    sm.red[0][tg][2 * cp] = mx0; sm.red[0][tg][2 * cp + 1] = mx1;
-    sm.red[1][tg][2 * cp] = mn0; sm.red[1][tg][2 * cp + 1] = mn1;
-    sm.red[2][tg][2 * cp] = s0;  sm.red[2][tg][2 * cp + 1] = s1;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float mx = -INFINITY, mn = INFINITY, sum = 0.f;
+    __syncthreads();
+    if (tid < D) {
+      float mx = -INFINITY, mn = INFINITY, sum = 0.f;
 #pragma unroll
-    for (int g = 0; g < NTG; ++g) {
-      mx = fmaxf(mx, sm.red[0][g][tid]);
-      mn = fminf(mn, sm.red[1][g][tid]);
-      sum += sm.red[2][g][tid];
+      for (int g = 0; g < NTG; ++g) {
+        mx = fmaxf(mx, sm.red[0][g][tid]);
+        mn = fminf(mn, sm.red[1][g][tid]);
+        sum += sm.red[2][g][tid];
+      }
+      sm.u[n][tid] = mx;
+      sm.u[n][D + tid] = mn;
+      sm.u[n][2 * D + tid] = sum / static_cast<float>(BS);
     }
-    sm.u[tid] = mx;
-    sm.u[D + tid] = mn;
-    sm.u[2 * D + tid] = sum / static_cast<float>(BS);
+    __syncthreads();
   }
-  __syncthreads();
   if (tid < 256) {
+    // rows in groups of kRowsPerGroup, every W_k load of a group in flight
+    // before its first use (the per-row arithmetic and order are those of a
+    // plain row loop)
+    constexpr int kRowsPerGroup = 8;
+    constexpr int NQ = (3 * D / 2 + 63) / 64;  // 32-bit words per lane and row
     const int w = tid >> 6;
     const int lane = tid & 63;
-    for (int r = w; r < DG; r += 4) {
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(w_k_h + static_cast<int64_t>(r) * 3 * D);
-      float acc = 0.f;
-      for (int q2 = lane; q2 < 3 * D / 2; q2 += 64) {
-        const uint32_t wv = row[q2];
-        acc = fmaf(bf_lo(wv), sm.u[2 * q2], acc);
-        acc = fmaf(bf_hi(wv), sm.u[2 * q2 + 1], acc);
+    for (int r0 = w; r0 < DG; r0 += 4 * kRowsPerGroup) {
+      uint32_t wv[kRowsPerGroup][NQ];
+#pragma unroll
+      for (int i = 0; i < kRowsPerGroup; ++i) {
+        const int r = r0 + 4 * i;
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(w_k_h + static_cast<int64_t>(r) * 3 * D);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int q2 = lane + 64 * q;
+          wv[i][q] = (r < DG && q2 < 3 * D / 2) ? row[q2] : 0u;
+        }
       }
-      acc = wave_sum(acc);
-      if (lane == 0) sm.v[r] = acc;
+#pragma unroll
+      for (int i = 0; i < kRowsPerGroup; ++i) {
+        const int r = r0 + 4 * i;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          if (n < nblk) {
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              const int q2 = lane + 64 * q;
+              if (q2 < 3 * D / 2) {
+                acc = fmaf(bf_lo(wv[i][q]), sm.u[n][2 * q2], acc);
+                acc = fmaf(bf_hi(wv[i][q]), sm.u[n][2 * q2 + 1], acc);
+              }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0 && r < DG) sm.v[n][r] = acc;
+          }
+        }
+      }
     }
   }
   __syncthreads();
-  if (tid < DG / 2) {
+  for (int idx = tid; idx < nblk * (DG / 2); idx += blockDim.x) {
+    const int n = idx / (DG / 2);
+    const int i = idx - n * (DG / 2);  // = tid mod DG/2: wf is this row's frequency
     float olo, ohi;
-    rope_pair(static_cast<double>(j) * BS, wf, sm.v[tid], sm.v[tid + DG / 2], &olo, &ohi);
+    rope_pair(static_cast<double>(j0 + n) * BS, wf, sm.v[n][i], sm.v[n][i + DG / 2], &olo, &ohi);
     const uint16_t lo = f2bf(olo), hi = f2bf(ohi);
-    dst[tid] = lo;
-    dst[tid + DG / 2] = hi;
+    dst[n * DG + i] = lo;
+    dst[n * DG + i + DG / 2] = hi;
     if (lds_copy != nullptr) {
-      lds_copy[tid] = lo;
-      lds_copy[tid + DG / 2] = hi;
+      lds_copy[n * DG + i] = lo;
+      lds_copy[n * DG + i + DG / 2] = hi;
     }
   }
+}
+
+// One block's entry (compress_blocks with a single block).
+template <int D, int DG>
+__device__ void compress_block(CompressSmem<D, DG, 1>& sm, const uint16_t* keys, int64_t st,
+                               int BS, const uint16_t* w_k_h, double wf, int j, uint16_t* dst,
+                               uint16_t* lds_copy = nullptr) {
+  compress_blocks<D, DG, 1>(sm, keys, st, BS, w_k_h, wf, j, 1, dst, lds_copy);
 }
 
 }  // namespace seer
