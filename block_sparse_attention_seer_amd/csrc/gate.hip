@@ -11,15 +11,16 @@
 // Kernels:
 //   prep_kernel    cache-entry tasks of the staged update: one newly
 //                  completed block of one (sequence, KV head) each (pool,
-//                  W_k GEMV, RoPE, bf16); prep_bulk_kernel does eight
+//                  W_k GEMV, RoPE, bf16); prep_bulk_kernel does sixteen
 //                  consecutive blocks per workgroup for large updates.
 //   commit_kernel  raises kcomp_lens once every new entry is written.
 //   gate_kernel    one 512-thread workgroup per (sequence, KV head): the
 //                  pair's new cache entries (fused step), its gate query
 //                  (MFMA GEMV + RoPE), its block logits (MFMA) and -- in the
 //                  fused step -- the selection, all without leaving the
-//                  workgroup.  Every global load it needs is issued at its
-//                  start, so the W_q, query and cache-row latencies overlap.
+//                  workgroup.  Every global load of the scoring is issued
+//                  up front, so the W_q, query and cache-row latencies
+//                  overlap.
 #include <cmath>
 
 #include "gate_dev.hpp"
@@ -82,10 +83,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 }
 
 // Bulk variant (a prompt's cache, or any update of many blocks): one
-// workgroup per kBulkBlocks consecutive new entries of one pair, so each W_k
-// row is read once for all of them.  The entries are bit-identical to the
-// one-block kernel's.
-constexpr int kBulkBlocks = 8;
+// workgroup per kBulkBlocks consecutive new entries of one pair, one MFMA
+// column each, so W_k is read once for all of them.  The entries are
+// bit-identical to the one-block kernel's.
+constexpr int kBulkBlocks = 16;
 
 template <int D, int DG>
 __global__ __launch_bounds__(256) void prep_bulk_kernel(PrepParams p) {
@@ -155,19 +156,6 @@ struct GateParams {
   RopeFreqs freqs;
 };
 
-// Part m (0, 1, 2) of the exact three-way bf16 split x = q0 + q1 + q2 (+ a
-// remainder below 2^-24 |x|): q0 = bf16(x), q1 = bf16(x - q0), q2 =
-// bf16(x - q0 - q1).  Each subtraction is exact in float32 (the operands
-// agree in their leading bits).
-__device__ __forceinline__ uint32_t bf16_part(float x, int m) {
-  const uint16_t h0 = f2bf(x);
-  const float r1 = x - __uint_as_float(static_cast<uint32_t>(h0) << 16);
-  const uint16_t h1 = f2bf(r1);
-  const float r2 = r1 - __uint_as_float(static_cast<uint32_t>(h1) << 16);
-  const uint16_t h2 = f2bf(r2);
-  return m == 0 ? h0 : (m == 1 ? h1 : h2);
-}
-
 // Chunk group c0 .. c0+kQueryChunks-1 (128 dims each) of this lane's W_q
 // pieces (B operand, tiles of 4 rows) and query pieces (A operand).
 template <int TQ>
@@ -234,7 +222,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   __shared__ float s_part[kGateRows][4];         // part sums (gate query, then logits)
   __shared__ float s_qg[DG];                     // the gate query
   __shared__ uint16_t s_new[kMaxInlineNew][DG];  // this launch's new cache entries
-  __shared__ CompressSmem<D, DG> s_cm;
+  __shared__ CompressSmem<D, DG, kMaxInlineNew> s_cm;
 
   const int pair = blockIdx.x;
   const int b = pair / p.Hkv;
@@ -254,7 +242,17 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   select_smem_init(s_sel);
   const double wf = p.freqs.w[tid % (DG / 2)];
 
-  // ---- all loads first: W_q rows and the query heads (first chunk group),
+  // ---- new cache entries (blocks completed since the last update), in one
+  // pass before anything else is in flight (they are rare: one step in b)
+  if (nnew > 0) {
+    const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(nc0) * p.BS * p.st;
+    compress_blocks<D, DG, kMaxInlineNew>(s_cm, keys, p.st, p.BS,
+                                          p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf, nc0,
+                                          nnew, p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + nc0) * DG,
+                                          &s_new[0][0]);
+  }
+
+  // ---- then all loads: W_q rows and the query heads (first chunk group),
   // then the first pass of cache rows
   const int K = p.G * D;  // W_q row length
   const int nch = (K + 127) / 128;
@@ -268,15 +266,6 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   const int passes = max(1, (nc + kGateRows - 1) / kGateRows);
   uint4 kv[TPW];  // rows already cached; this launch's entries come from LDS
   load_rows<TPW, RPT, P, DG>(kv, kc, w * RPW, nc0, n);
-
-  // ---- new cache entries (blocks completed since the last update)
-  for (int e = 0; e < nnew; ++e) {
-    const int j = nc0 + e;
-    const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j) * p.BS * p.st;
-    compress_block<D, DG>(s_cm, keys, p.st, p.BS, p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf,
-                          j, p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j) * DG, s_new[e]);
-    __syncthreads();  // s_cm is reused by the next entry
-  }
 
   // ---- gate query: y = W_q[h] x, then RoPE at position L-1
   {

@@ -51,106 +51,124 @@ __device__ __forceinline__ void rope_pair(double pos, double w, float lo, float 
 // Shared-memory scratch of the cache-entry computation of up to NB blocks.
 template <int D, int DG, int NB = 1>
 struct CompressSmem {
+  static_assert(NB >= 1 && NB <= 16, "one MFMA column per block");
   static constexpr int CP = D / 2;      // channel pairs
   static constexpr int NTG = 256 / CP;  // token groups
-  float red[3][NTG][D];
-  float u[NB][3 * D];
-  float v[NB][DG];
+  float red[2][3][NTG][D];              // pooling partials of two blocks
+  float u[NB][3 * D + 4];               // pooled features (rows padded: no bank conflicts)
+  float v[NB][DG];                      // W_k u
 };
 
 // K Compression Cache entries of blocks j0 .. j0+nblk-1 (nblk <= NB,
 // consecutive blocks of one pair; keys points at row 0 of block j0, dst at
 // entry j0) computed by the first 256 threads of the workgroup; every thread
-// of the workgroup must call this (it contains barriers).  Each block's
-// arithmetic is the same for every NB and nblk, so an entry has the same bits
-// whichever way the cache is built.
-//   pooling, block by block: each (channel pair, token group) thread reduces
-//   a strided set of tokens, then threads < D fold the groups in a fixed
-//   order;
-//   GEMV: wave w of the 256 handles rows w, w+4, ... (loaded 8 rows at a
-//   time, each row applied to every block); lanes split the 3d columns and
-//   reduce across the wave;
+// of the workgroup must call this (it contains barriers).  A block's
+// arithmetic does not depend on NB or nblk (MFMA columns are independent),
+// so an entry has the same bits whichever way the cache is built.
+//   pooling, two blocks at a time: each (channel pair, token group) thread
+//   loads its strided tokens of both blocks, then reduces them in token
+//   order; threads < D fold the groups in a fixed order;
+//   GEMV on MFMA: V[row][block] = W_k[row][:] . u[block][:], the blocks as
+//   the 16 B-operand columns; max and min features are exact in bf16, the
+//   mean enters as three bf16 components against the same W_k columns;
 //   RoPE at position j*b (float64 angle), bf16 store (round to nearest even)
 //   to dst and, when lds_copy is not null, to LDS ([NB][DG]) as well.
 //   wf is this thread's RoPE frequency, theta^(-2(t mod DG/2)/DG) for thread t.
 template <int D, int DG, int NB>
-__device__ void compress_blocks(CompressSmem<D, DG, NB>& sm, const uint16_t* keys, int64_t st,
-                                int BS, const uint16_t* w_k_h, double wf, int j0, int nblk,
-                                uint16_t* dst, uint16_t* lds_copy = nullptr) {
+__device__ __forceinline__ void compress_blocks(CompressSmem<D, DG, NB>& sm, const uint16_t* keys,
+                                                int64_t st, int BS, const uint16_t* w_k_h,
+                                                double wf, int j0, int nblk, uint16_t* dst,
+                                                uint16_t* lds_copy = nullptr) {
   constexpr int CP = CompressSmem<D, DG, NB>::CP;
   constexpr int NTG = CompressSmem<D, DG, NB>::NTG;
+  constexpr int TMAX = 128 / NTG;  // tokens per thread at b <= 128
   const int tid = threadIdx.x;
-  for (int n = 0; n < nblk; ++n) {
+  for (int n0 = 0; n0 < nblk; n0 += 2) {
     if (tid < 256) {
       const int cp = tid % CP;
       const int tg = tid / CP;
-      const uint16_t* base = keys + static_cast<int64_t>(n) * BS * st + 2 * cp;
-      float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY, s0 = 0.f, s1 = 0.f;
-      for (int t = tg; t < BS; t += NTG) {
-        const uint32_t wv = *reinterpret_cast<const uint32_t*>(base + t * st);
-        const float a = bf_lo(wv), bb = bf_hi(wv);
-        mx0 = fmaxf(mx0, a); mn0 = fminf(mn0, a); s0 += a;
-        mx1 = fmaxf(mx1, bb); mn1 = fminf(mn1, bb); s1 += bb;
+      const int cnt = (BS - tg + NTG - 1) / NTG;  // this thread's tokens of a block
+      uint32_t wv[2][TMAX];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        const uint16_t* base = keys + static_cast<int64_t>(n0 + pb) * BS * st + 2 * cp;
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i)
+          wv[pb][i] = (n0 + pb < nblk && i < cnt)
+                          ? *reinterpret_cast<const uint32_t*>(base + (tg + NTG * i) * st)
+                          : 0u;
       }
-      sm.red[0][tg][2 * cp] = mx0; sm.red[0][tg][2 * cp + 1] = mx1;
-      sm.red[1][tg][2 * cp] = mn0; sm.red[1][tg][2 * cp + 1] = mn1;
-      sm.red[2][tg][2 * cp] = s0;  sm.red[2][tg][2 * cp + 1] = s1;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY, s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+          if (i < cnt) {
+            const float a = bf_lo(wv[pb][i]), bb = bf_hi(wv[pb][i]);
+            mx0 = fmaxf(mx0, a); mn0 = fminf(mn0, a); s0 += a;
+            mx1 = fmaxf(mx1, bb); mn1 = fminf(mn1, bb); s1 += bb;
+          }
+        }
+        sm.red[pb][0][tg][2 * cp] = mx0; sm.red[pb][0][tg][2 * cp + 1] = mx1;
+        sm.red[pb][1][tg][2 * cp] = mn0; sm.red[pb][1][tg][2 * cp + 1] = mn1;
+        sm.red[pb][2][tg][2 * cp] = s0;  sm.red[pb][2][tg][2 * cp + 1] = s1;
+      }
     }
     __syncthreads();
     if (tid < D) {
-      float mx = -INFINITY, mn = INFINITY, sum = 0.f;
+      for (int pb = 0; pb < 2 && n0 + pb < nblk; ++pb) {
+        float mx = -INFINITY, mn = INFINITY, sum = 0.f;
 #pragma unroll
-      for (int g = 0; g < NTG; ++g) {
-        mx = fmaxf(mx, sm.red[0][g][tid]);
-        mn = fminf(mn, sm.red[1][g][tid]);
-        sum += sm.red[2][g][tid];
+        for (int g = 0; g < NTG; ++g) {
+          mx = fmaxf(mx, sm.red[pb][0][g][tid]);
+          mn = fminf(mn, sm.red[pb][1][g][tid]);
+          sum += sm.red[pb][2][g][tid];
+        }
+        sm.u[n0 + pb][tid] = mx;
+        sm.u[n0 + pb][D + tid] = mn;
+        sm.u[n0 + pb][2 * D + tid] = sum / static_cast<float>(BS);
       }
-      sm.u[n][tid] = mx;
-      sm.u[n][D + tid] = mn;
-      sm.u[n][2 * D + tid] = sum / static_cast<float>(BS);
     }
     __syncthreads();
   }
   if (tid < 256) {
-    // rows in groups of kRowsPerGroup, every W_k load of a group in flight
-    // before its first use (the per-row arithmetic and order are those of a
-    // plain row loop)
-    constexpr int kRowsPerGroup = 8;
-    constexpr int NQ = (3 * D / 2 + 63) / 64;  // 32-bit words per lane and row
+    constexpr int TW = DG / 64;  // 16-row tiles per wave
+    constexpr int KS1 = D / 32;  // k-steps per feature section
     const int w = tid >> 6;
     const int lane = tid & 63;
-    for (int r0 = w; r0 < DG; r0 += 4 * kRowsPerGroup) {
-      uint32_t wv[kRowsPerGroup][NQ];
+    const int n = lane & 15;  // A row / B column (block)
+    const int g = lane >> 4;
+    uint4 a[TW][3 * KS1];  // this lane's W_k pieces: row (w*TW + t)*16 + n
 #pragma unroll
-      for (int i = 0; i < kRowsPerGroup; ++i) {
-        const int r = r0 + 4 * i;
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(w_k_h + static_cast<int64_t>(r) * 3 * D);
+    for (int t = 0; t < TW; ++t) {
+      const uint16_t* row = w_k_h + static_cast<int64_t>((w * TW + t) * 16 + n) * 3 * D + 8 * g;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int q2 = lane + 64 * q;
-          wv[i][q] = (r < DG && q2 < 3 * D / 2) ? row[q2] : 0u;
-        }
+      for (int s = 0; s < 3 * KS1; ++s) a[t][s] = ld16(row + 32 * s);
+    }
+    f32x4_t acc[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 5 * KS1; ++s) {  // max, min, then the mean's three components
+      const int sec = s / KS1;
+      const int as = (sec < 2 ? sec : 2) * KS1 + s % KS1;  // W_k k-step
+      uint4 bop = make_uint4(0u, 0u, 0u, 0u);
+      if (n < nblk) {
+        const float* x = &sm.u[n][32 * as + 8 * g];
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = sec < 2 ? f2bf(x[i]) : bf16_part(x[i], sec - 2);
+        bop = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16));
       }
 #pragma unroll
-      for (int i = 0; i < kRowsPerGroup; ++i) {
-        const int r = r0 + 4 * i;
+      for (int t = 0; t < TW; ++t) acc[t] = mfma16x16x32(a[t][as], bop, acc[t]);
+    }
+    if (n < nblk) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          if (n < nblk) {
-            float acc = 0.f;
+      for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-              const int q2 = lane + 64 * q;
-              if (q2 < 3 * D / 2) {
-                acc = fmaf(bf_lo(wv[i][q]), sm.u[n][2 * q2], acc);
-                acc = fmaf(bf_hi(wv[i][q]), sm.u[n][2 * q2 + 1], acc);
-              }
-            }
-            acc = wave_sum(acc);
-            if (lane == 0 && r < DG) sm.v[n][r] = acc;
-          }
-        }
-      }
+        for (int r = 0; r < 4; ++r) sm.v[n][(w * TW + t) * 16 + 4 * g + r] = acc[t][r];
     }
   }
   __syncthreads();

@@ -42,6 +42,20 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// Part m (0, 1, 2) of the exact three-way bf16 split x = q0 + q1 + q2 (+ a
+// remainder below 2^-24 |x|): q0 = bf16(x), q1 = bf16(x - q0), q2 =
+// bf16(x - q0 - q1).  Each subtraction is exact in float32 (the operands
+// agree in their leading bits).  bf16 x bf16 products are exact in float32,
+// so an MFMA over the three parts keeps float32 accuracy.
+__device__ __forceinline__ uint32_t bf16_part(float x, int m) {
+  const uint16_t h0 = f2bf(x);
+  const float r1 = x - __uint_as_float(static_cast<uint32_t>(h0) << 16);
+  const uint16_t h1 = f2bf(r1);
+  const float r2 = r1 - __uint_as_float(static_cast<uint32_t>(h1) << 16);
+  const uint16_t h2 = f2bf(r2);
+  return m == 0 ? h0 : (m == 1 ? h1 : h2);
+}
+
 // Order-preserving map of a float to an unsigned key (larger float, larger
 // key).  -0 is mapped like +0 and NaN below every number.
 __device__ __forceinline__ uint32_t float_key(float z) {
