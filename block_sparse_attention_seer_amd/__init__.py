@@ -32,7 +32,8 @@ __all__ = [
     "SELECT_TOPK", "SELECT_THRESHOLD", "SELECT_TOPP", "make_dims",
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
-    "seer_sparse_decode", "seer_dense_decode", "seer_decode_step_workspace_bytes",
+    "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
+    "seer_dense_decode_paged", "seer_decode_step_workspace_bytes",
     "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
     "DecodeStep",
 ]
@@ -48,7 +49,8 @@ SELECT_TOPP = 3  # threshold carries the mass p
 EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
-    "seer_sparse_decode", "seer_dense_decode", "seer_decode_step_workspace_bytes",
+    "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
+    "seer_dense_decode_paged", "seer_decode_step_workspace_bytes",
     "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
 )
 
@@ -98,6 +100,12 @@ _SIGS = {
                                   ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
     "seer_dense_decode": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, ctypes.c_float, _I32,
                                  _P, ctypes.c_size_t, _P, _P, _P]),
+    "seer_sparse_decode_paged": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, ctypes.c_int64,
+                                        ctypes.c_int64, _I32, _P, _I32, _P, _P, _P, _I32,
+                                        ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
+    "seer_dense_decode_paged": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, ctypes.c_int64,
+                                       ctypes.c_int64, _I32, _P, _I32, _P, ctypes.c_float, _I32,
+                                       _P, ctypes.c_size_t, _P, _P, _P]),
     "seer_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SeerDims), _I32, _I32]),
     "seer_decode_step": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _I32, ctypes.c_double, _I32, _I32, ctypes.c_float, _I32, _P, _P,
@@ -287,6 +295,54 @@ def seer_dense_decode(dims: SeerDims, q, k_cache, v_cache, seq_lens, scale: floa
     _check(lib().seer_dense_decode(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(seq_lens), float(scale), int(num_split), wp, wn, _ptr(out),
                                    _ptr(lse), _stream(q)), "seer_dense_decode")
+
+
+def _check_pages(dims: SeerDims, q, k_pages, v_pages, block_table, seq_lens, out, lse):
+    """Page pools [num_pages, H_kv, b, d] bf16 (contiguous) and the block table
+    [B, table_stride] int32; returns (num_pages, page_stride, page_head_stride,
+    table_stride)."""
+    B, Hq, Hkv, d, bs = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim, dims.block_size
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, Hq, d), dev)
+    if not isinstance(k_pages, torch.Tensor) or k_pages.dim() != 4:
+        raise ValueError("k_pages must be a [num_pages, H_kv, block_size, d] tensor")
+    num_pages = k_pages.shape[0]
+    _need(k_pages, "k_pages", torch.bfloat16, (num_pages, Hkv, bs, d), dev)
+    _need(v_pages, "v_pages", torch.bfloat16, (num_pages, Hkv, bs, d), dev)
+    if dims.kv_stride_t != d:
+        raise ValueError("paged decode: dims.kv_stride_t must be head_dim (rows of a page)")
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
+        raise ValueError("block_table must be a [B, table_stride] int32 tensor")
+    _need(block_table, "block_table", torch.int32, (B, block_table.shape[1]), dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    _need(out, "out", torch.bfloat16, (B, Hq, d), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq), dev)
+    return num_pages, Hkv * bs * d, bs * d, block_table.shape[1]
+
+
+def seer_sparse_decode_paged(dims: SeerDims, q, k_pages, v_pages, block_table, seq_lens,
+                             block_idx, num_selected, max_selected: int, scale: float,
+                             num_split: int, workspace, out, lse=None) -> None:
+    npg, ps, phs, ts = _check_pages(dims, q, k_pages, v_pages, block_table, seq_lens, out, lse)
+    dev = q.device
+    _need(block_idx, "block_idx", torch.int32, (dims.batch, dims.num_kv_heads, max_selected), dev)
+    _need(num_selected, "num_selected", torch.int32, (dims.batch, dims.num_kv_heads), dev)
+    wp, wn = _ws(workspace, dev)
+    _check(lib().seer_sparse_decode_paged(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages), ps, phs, npg, _ptr(block_table),
+        ts, _ptr(seq_lens), _ptr(block_idx), _ptr(num_selected), int(max_selected), float(scale),
+        int(num_split), wp, wn, _ptr(out), _ptr(lse), _stream(q)), "seer_sparse_decode_paged")
+
+
+def seer_dense_decode_paged(dims: SeerDims, q, k_pages, v_pages, block_table, seq_lens,
+                            scale: float, num_split: int, workspace, out, lse=None) -> None:
+    npg, ps, phs, ts = _check_pages(dims, q, k_pages, v_pages, block_table, seq_lens, out, lse)
+    wp, wn = _ws(workspace, q.device)
+    _check(lib().seer_dense_decode_paged(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages), ps, phs, npg, _ptr(block_table),
+        ts, _ptr(seq_lens), float(scale), int(num_split), wp, wn, _ptr(out), _ptr(lse), _stream(q)),
+        "seer_dense_decode_paged")
 
 
 def seer_decode_step_workspace_bytes(dims: SeerDims, max_selected: int, num_split: int = 0) -> int:

@@ -26,6 +26,10 @@
 //     token) and the B operand (8 tokens of one dim) is assembled with
 //     byte permutes, so V never goes through LDS.  All K and V loads of a
 //     chunk (32 KiB per wave at d = 128) are in flight together;
+//   * a paged cache (one block per page) changes only where a chunk's rows
+//     start: the workgroup stages its sequence's block-table row in LDS with
+//     the index row, and an out-of-range page is skipped like an invalid
+//     index entry;
 //   * the waves of a split merge in LDS; with one split the workgroup writes
 //     the output directly.  Otherwise each split writes an (lse, o) partial
 //     with device-coherent stores, counts itself on a per-(b, h) counter,
@@ -42,7 +46,8 @@ namespace seer {
 
 namespace {
 
-constexpr int kIdxLds = 512;  // index-row entries staged in LDS per workgroup
+constexpr int kIdxLds = 512;     // index-row entries staged in LDS per workgroup
+constexpr int kTableLds = 2048;  // paged cache: block-table entries staged in LDS
 // 16-token tiles per chunk (2 or 4).  Measured on MI355X: 4 (32 KiB of K
 // and V in flight per wave at d = 128) streams faster than 2, whose finer
 // share per wave does not make up for the halved bytes in flight.
@@ -69,6 +74,11 @@ struct DecodeParams {
   // fused step: workgroup 0 raises the cache counters of every sequence
   int32_t* commit_lens;
   int commit_max_new, B, BS, NBmax;
+  // paged cache: the page of block j of sequence b is
+  // block_table[b * table_stride + j]; a page holds H_kv x b rows of d
+  const int32_t* block_table;
+  int table_stride, num_pages;
+  int64_t page_stride, page_head_stride;
 };
 
 // bf16 j (0..3) of a's four values in the low half, of b's in the high half.
@@ -78,7 +88,7 @@ __device__ __forceinline__ uint32_t pick2(uint2 a, uint2 b, int j) {
   return (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
 }
 
-template <int D, int BS, bool DENSE, int NW>
+template <int D, int BS, bool DENSE, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   constexpr int TPC = kTilesPerChunk;  // 16-token tiles per chunk
   constexpr int KS = D / 32;   // k-steps of the score contraction
@@ -114,6 +124,11 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   __shared__ int s_idx[kIdxLds];
   if (!DENSE)
     for (int i = tid; i < min(p.max_sel, kIdxLds); i += NW * 64) s_idx[i] = idx[i];
+  // paged cache: this sequence's block-table row, requested with the rest
+  __shared__ int s_table[PAGED ? kTableLds : 1];
+  if (PAGED)
+    for (int i = tid; i < min(p.table_stride, kTableLds); i += NW * 64)
+      s_table[i] = p.block_table[static_cast<int64_t>(b) * p.table_stride + i];
 
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.Lmax);
@@ -160,6 +175,21 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     const int blk = DENSE ? slot : (slot < kIdxLds ? s_idx[slot] : idx[slot]);
     const int base = blk * BS + (c - slot * CPB) * (16 * TPC);
     if (blk < 0 || blk >= nblk || base >= L) continue;  // invalid entry: skipped
+    // row 0 of the chunk's block in the cache
+    const uint16_t* kc;
+    const uint16_t* vc;
+    if constexpr (PAGED) {
+      if (blk >= p.table_stride) continue;
+      const int page = blk < kTableLds
+                           ? s_table[blk]
+                           : p.block_table[static_cast<int64_t>(b) * p.table_stride + blk];
+      if (page < 0 || page >= p.num_pages) continue;  // invalid page: skipped as well
+      kc = p.k + page * p.page_stride + h * p.page_head_stride;
+      vc = p.v + page * p.page_stride + h * p.page_head_stride;
+    } else {
+      kc = kb + static_cast<int64_t>(blk) * BS * p.st;
+      vc = vb + static_cast<int64_t>(blk) * BS * p.st;
+    }
     // first token of each of the chunk's tiles, or -1 past the sequence
     int tok0[TPC];
 #pragma unroll
@@ -170,8 +200,8 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int nt = 0; nt < TPC; ++nt) {
       if (tok0[nt] >= 0) {
-        const int row = min(tok0[nt] + ln, last);
-        const uint16_t* kp = kb + row * p.st + 8 * lq;
+        const int row = min(tok0[nt] + ln, last) - blk * BS;  // within the block
+        const uint16_t* kp = kc + row * p.st + 8 * lq;
 #pragma unroll
         for (int s = 0; s < KS; ++s) kr[nt][s] = ld16(kp + 32 * s);
       } else {
@@ -186,8 +216,8 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (tok0[nt] >= 0) {
-          const int row = min(tok0[nt] + 4 * lq + r, last);
-          const uint16_t* vp = vb + row * p.st + 4 * ln;
+          const int row = min(tok0[nt] + 4 * lq + r, last) - blk * BS;
+          const uint16_t* vp = vc + row * p.st + 4 * ln;
 #pragma unroll
           for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = ld8(vp + 64 * hh);
         } else {
@@ -484,23 +514,24 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
   }
 }
 
-template <int D, int BS, bool DENSE, int NW>
+template <int D, int BS, bool DENSE, int NW, bool PAGED>
 void launch_one(const DecodeParams& p, int grid, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(NW) * p.G * D * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW>), dim3(grid), dim3(NW * 64), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW, PAGED>), dim3(grid), dim3(NW * 64), lds,
+                     stream, p);
 }
 
-template <int NW>
+template <int NW, bool PAGED>
 void launch_variant(int key, const DecodeParams& p, int grid, hipStream_t s) {
   switch (key) {
-    case 0: launch_one<64, 64, false, NW>(p, grid, s); break;
-    case 1: launch_one<64, 64, true, NW>(p, grid, s); break;
-    case 2: launch_one<64, 128, false, NW>(p, grid, s); break;
-    case 3: launch_one<64, 128, true, NW>(p, grid, s); break;
-    case 4: launch_one<128, 64, false, NW>(p, grid, s); break;
-    case 5: launch_one<128, 64, true, NW>(p, grid, s); break;
-    case 6: launch_one<128, 128, false, NW>(p, grid, s); break;
-    default: launch_one<128, 128, true, NW>(p, grid, s); break;
+    case 0: launch_one<64, 64, false, NW, PAGED>(p, grid, s); break;
+    case 1: launch_one<64, 64, true, NW, PAGED>(p, grid, s); break;
+    case 2: launch_one<64, 128, false, NW, PAGED>(p, grid, s); break;
+    case 3: launch_one<64, 128, true, NW, PAGED>(p, grid, s); break;
+    case 4: launch_one<128, 64, false, NW, PAGED>(p, grid, s); break;
+    case 5: launch_one<128, 64, true, NW, PAGED>(p, grid, s); break;
+    case 6: launch_one<128, 128, false, NW, PAGED>(p, grid, s); break;
+    default: launch_one<128, 128, true, NW, PAGED>(p, grid, s); break;
   }
 }
 
@@ -534,6 +565,11 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   p.B = d.batch;
   p.BS = d.block_size;
   p.NBmax = static_cast<int>(nb_max(&d));
+  p.block_table = a.block_table;
+  p.table_stride = a.table_stride;
+  p.num_pages = a.num_pages;
+  p.page_stride = a.page_stride;
+  p.page_head_stride = a.page_head_stride;
   const bool inline_merge = a.merge_inline;
   if (S > 1) {
     char* ws = static_cast<char*>(a.workspace);
@@ -558,10 +594,11 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   const int nw = ((wpg == 4 || wpg == 8) && decode_waves_fit(wpg, G, d.head_dim))
                      ? wpg
                      : decode_waves_per_group(G, d.head_dim);
+  const bool paged = a.block_table != nullptr;
   if (nw == 8)
-    launch_variant<8>(key, p, grid, s);
+    paged ? launch_variant<8, true>(key, p, grid, s) : launch_variant<8, false>(key, p, grid, s);
   else
-    launch_variant<4>(key, p, grid, s);
+    paged ? launch_variant<4, true>(key, p, grid, s) : launch_variant<4, false>(key, p, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error(std::string("decode launch: ") + hipGetErrorString(e));

@@ -191,12 +191,37 @@ int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks, int32_t num
   return SEER_OK;
 }
 
+// A paged cache: page pools and the block table (see seer_sparse_decode_paged).
+struct PagedCache {
+  const int32_t* block_table;
+  int32_t table_stride;
+  int32_t num_pages;
+  int64_t page_stride;
+  int64_t page_head_stride;
+};
+
+static int check_paged(const seer_dims* dims, const PagedCache& pc, std::string* why) {
+  if (check_ptr(pc.block_table, 4, "block_table", why) != SEER_OK) return SEER_ERR_INVALID_ARG;
+  if (pc.table_stride < 1 || pc.num_pages < 1) {
+    *why = "table_stride and num_pages must be >= 1";
+    return SEER_ERR_INVALID_ARG;
+  }
+  if (pc.page_stride < 1 || pc.page_head_stride < 0 || (pc.page_stride % 8) ||
+      (pc.page_head_stride % 8)) {
+    *why = "page strides must be positive multiples of 8 elements";
+    return SEER_ERR_INVALID_ARG;
+  }
+  (void)dims;
+  return SEER_OK;
+}
+
 static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* seq_lens, const int32_t* block_idx,
                          const int32_t* num_selected, int32_t max_blocks, float scale,
                          int32_t num_split, void* workspace, size_t workspace_bytes,
                          uint16_t* out, float* lse, void* stream,
-                         int32_t* commit_lens = nullptr, int commit_max_new = 0) {
+                         int32_t* commit_lens = nullptr, int commit_max_new = 0,
+                         const PagedCache* paged = nullptr) {
   SEER_CHECK(check_dims(dims, &why_));
   SEER_CHECK(check_ptr(q, 16, "q", &why_));
   SEER_CHECK(check_ptr(k, 16, "k_cache", &why_));
@@ -221,6 +246,14 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
   seer::DecodeArgs a{q, k, v, seq_lens, block_idx, num_selected, max_blocks, scale, s,
                      tuning_waves(), tuning_merge_inline(), workspace, out, lse,
                      commit_lens, commit_max_new};
+  if (paged != nullptr) {
+    SEER_CHECK(check_paged(dims, *paged, &why_));
+    a.block_table = paged->block_table;
+    a.table_stride = paged->table_stride;
+    a.num_pages = paged->num_pages;
+    a.page_stride = paged->page_stride;
+    a.page_head_stride = paged->page_head_stride;
+  }
   return seer::launch_decode(*dims, a, stream);
 }
 
@@ -244,6 +277,36 @@ int seer_dense_decode(const seer_dims* dims, const uint16_t* q, const uint16_t* 
   return decode_common(dims, q, k_cache, v_cache, seq_lens, nullptr, nullptr,
                        static_cast<int32_t>(seer::nb_max(dims)), scale, num_split, workspace,
                        workspace_bytes, out, lse, stream);
+}
+
+int seer_sparse_decode_paged(const seer_dims* dims, const uint16_t* q, const uint16_t* k_pages,
+                             const uint16_t* v_pages, int64_t page_stride,
+                             int64_t page_head_stride, int32_t num_pages,
+                             const int32_t* block_table, int32_t table_stride,
+                             const int32_t* seq_lens, const int32_t* block_idx,
+                             const int32_t* num_selected, int32_t max_selected, float scale,
+                             int32_t num_split, void* workspace, size_t workspace_bytes,
+                             uint16_t* out, float* lse, void* stream) {
+  SEER_CHECK(check_ptr(block_idx, 4, "block_idx", &why_));
+  SEER_CHECK(check_ptr(num_selected, 4, "num_selected", &why_));
+  const PagedCache pc{block_table, table_stride, num_pages, page_stride, page_head_stride};
+  return decode_common(dims, q, k_pages, v_pages, seq_lens, block_idx, num_selected, max_selected,
+                       scale, num_split, workspace, workspace_bytes, out, lse, stream, nullptr, 0,
+                       &pc);
+}
+
+int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint16_t* k_pages,
+                            const uint16_t* v_pages, int64_t page_stride, int64_t page_head_stride,
+                            int32_t num_pages, const int32_t* block_table, int32_t table_stride,
+                            const int32_t* seq_lens, float scale, int32_t num_split,
+                            void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                            void* stream) {
+  std::string why;
+  if (check_dims(dims, &why) != SEER_OK) return fail(check_dims(dims, &why), why);
+  const PagedCache pc{block_table, table_stride, num_pages, page_stride, page_head_stride};
+  return decode_common(dims, q, k_pages, v_pages, seq_lens, nullptr, nullptr,
+                       static_cast<int32_t>(seer::nb_max(dims)), scale, num_split, workspace,
+                       workspace_bytes, out, lse, stream, nullptr, 0, &pc);
 }
 
 int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16_t* q,

@@ -110,6 +110,12 @@ struct DecodeArgs {
   float* lse;
   int32_t* commit_lens;         // fused step: raise kcomp_lens here (or nullptr)
   int commit_max_new;
+  // paged cache (k, v are page pools) when block_table != nullptr
+  const int32_t* block_table;
+  int table_stride;
+  int num_pages;
+  int64_t page_stride;
+  int64_t page_head_stride;
 };
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
 

@@ -249,6 +249,45 @@ int seer_dense_decode(const seer_dims* dims, const uint16_t* q,
                       float* lse, void* stream);
 
 /*
+ * seer_sparse_decode_paged / seer_dense_decode_paged -- the decodes above on
+ * a paged KV cache.
+ *
+ * [CP Knowl 14] names PagedAttention support as needed for serving.  The
+ * cache is a pool of pages of b tokens (one block per page); logical block j
+ * of sequence b lives in page block_table[b * table_stride + j].  Only where
+ * a block's rows are read changes; results are bit-identical to the
+ * contiguous call on the same rows.
+ *
+ *   k_pages, v_pages  page pools, bf16: row t (0 <= t < b) of head h in page
+ *                     p starts at element p*page_stride + h*page_head_stride
+ *                     + t*dims.kv_stride_t and holds d contiguous values
+ *                     (e.g. [num_pages, H_kv, b, d]: page_head_stride = b*d,
+ *                     page_stride = H_kv*b*d, kv_stride_t = d).
+ *                     dims.kv_stride_b and kv_stride_h are not used.
+ *   num_pages         pages in the pool; a block whose page is outside
+ *                     [0, num_pages) is skipped like an invalid index entry.
+ *   block_table       [B, table_stride] int32 (device); entries of blocks
+ *                     0 .. ceil(L/b)-1 are read (a block >= table_stride is
+ *                     skipped).
+ * Strides are in elements, multiples of 8.  Everything else as
+ * seer_sparse_decode / seer_dense_decode.
+ */
+int seer_sparse_decode_paged(const seer_dims* dims, const uint16_t* q, const uint16_t* k_pages,
+                             const uint16_t* v_pages, int64_t page_stride,
+                             int64_t page_head_stride, int32_t num_pages,
+                             const int32_t* block_table, int32_t table_stride,
+                             const int32_t* seq_lens, const int32_t* block_idx,
+                             const int32_t* num_selected, int32_t max_selected, float scale,
+                             int32_t num_split, void* workspace, size_t workspace_bytes,
+                             uint16_t* out, float* lse, void* stream);
+int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint16_t* k_pages,
+                            const uint16_t* v_pages, int64_t page_stride, int64_t page_head_stride,
+                            int32_t num_pages, const int32_t* block_table, int32_t table_stride,
+                            const int32_t* seq_lens, float scale, int32_t num_split,
+                            void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                            void* stream);
+
+/*
  * seer_decode_step -- one whole decode step of one layer in three launches,
  * with the same results as seer_kcomp_update (with max_new_blocks), then
  * seer_gate_scores, seer_select_blocks and seer_sparse_decode, in that order

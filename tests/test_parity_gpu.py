@@ -219,6 +219,174 @@ def test_decode_strided_kv_layout(S):
             assert_out_close(f64(out[b, h * g:(h + 1) * g]), o_ref, f"b={b} h={h}")
 
 
+# -------------------------------------------------------- paged KV cache
+
+def to_pages(k, v, bs, gen, extra_pages=3, table_pad=0):
+    """Scatter a contiguous [B, H, Lmax, d] cache into a pool of pages
+    [num_pages, H, bs, d] in a random order; returns the pools and the block
+    table [B, nbm + table_pad] (pad columns -1).  Unused pages hold NaN."""
+    B, H, lmax, d = k.shape
+    nbm = -(-lmax // bs)
+    num_pages = B * nbm + extra_pages
+    perm = torch.randperm(num_pages, generator=gen)[: B * nbm].view(B, nbm)
+    kp = torch.full((num_pages, H, bs, d), float("nan"), dtype=torch.bfloat16)
+    vp = torch.full((num_pages, H, bs, d), float("nan"), dtype=torch.bfloat16)
+    for b in range(B):
+        for j in range(nbm):
+            t0, t1 = j * bs, min((j + 1) * bs, lmax)
+            kp[perm[b, j], :, : t1 - t0] = k[b, :, t0:t1]
+            vp[perm[b, j], :, : t1 - t0] = v[b, :, t0:t1]
+    table = torch.full((B, nbm + table_pad), -1, dtype=torch.int32)
+    table[:, :nbm] = perm.to(torch.int32)
+    return kp, vp, table
+
+
+def random_selection(lens, bs, Hkv, max_sel, rng):
+    B = len(lens)
+    idx = np.full((B, Hkv, max_sel), -1, dtype=np.int32)
+    nsel = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        total = -(-lens[b] // bs)
+        for h in range(Hkv):
+            n = int(rng.integers(0, min(total, max_sel) + 1))
+            chosen = sorted(rng.choice(total, size=n, replace=False).tolist()) if n else []
+            idx[b, h, :n] = chosen
+            nsel[b, h] = n
+    return idx, nsel
+
+
+PAGED_CASES = [
+    # d, bs, Hq, Hkv, lens, table_pad
+    (128, 64, 40, 8, [4096, 700, 1], 0),
+    (128, 128, 32, 8, [2000, 129], 5),
+    (64, 64, 8, 2, [300, 64, 65], 1),
+    (128, 64, 4, 1, [2048 * 64 + 1000], 0),  # block table longer than the kernel's LDS copy
+]
+
+
+@pytest.mark.parametrize("d,bs,Hq,Hkv,lens,table_pad", PAGED_CASES)
+def test_paged_decode_equals_contiguous(S, d, bs, Hq, Hkv, lens, table_pad):
+    say(f"paged decode d={d} bs={bs} Hq={Hq} Hkv={Hkv} lens={lens} pad={table_pad}")
+    B = len(lens)
+    lmax = max(lens) + 3
+    gen = torch.Generator().manual_seed(41 + d + bs + B)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16).to(DEV)
+    k, v = make_kv(B, Hkv, lmax, d, gen, poison_from=lens)
+    kp, vp, table = to_pages(k, v, bs, gen, table_pad=table_pad)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    nbm = dims.nb_max
+    max_sel = min(nbm, 600)
+    idx, nsel = random_selection(lens, bs, Hkv, max_sel, np.random.default_rng(d + bs))
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kd, vd, kpd, vpd, td = k.to(DEV), v.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV)
+    idx_d, nsel_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(nsel).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    for num_split in (1, 0):
+        ns = S.seer_decode_num_split(dims, nbm, num_split)
+        ws = torch.zeros(S.seer_decode_workspace_bytes(dims, nbm, ns) // 4 + 64,
+                         dtype=torch.float32, device=DEV)
+        res = {}
+        for name in ("contig", "paged"):
+            out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+            if name == "contig":
+                S.seer_sparse_decode(dims, q, kd, vd, seq, idx_d, nsel_d, max_sel, scale, ns, ws,
+                                     out, lse)
+            else:
+                S.seer_sparse_decode_paged(dims, q, kpd, vpd, td, seq, idx_d, nsel_d, max_sel,
+                                           scale, ns, ws, out, lse)
+            res[name + "_sparse"] = (out, lse)
+            out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+            if name == "contig":
+                S.seer_dense_decode(dims, q, kd, vd, seq, scale, ns, ws, out, lse)
+            else:
+                S.seer_dense_decode_paged(dims, q, kpd, vpd, td, seq, scale, ns, ws, out, lse)
+            res[name + "_dense"] = (out, lse)
+        torch.cuda.synchronize()
+        for kind in ("sparse", "dense"):
+            oc, lc = res["contig_" + kind]
+            op, lp = res["paged_" + kind]
+            assert torch.equal(oc.view(torch.int16), op.view(torch.int16)), f"{kind} out split={ns}"
+            assert torch.equal(lc.view(torch.int32), lp.view(torch.int32)), f"{kind} lse split={ns}"
+
+
+def test_paged_decode_skips_missing_pages(S):
+    say("paged decode with missing pages")
+    B, Hq, Hkv, d, bs = 2, 16, 4, 128, 64
+    lens = [1500, 900]
+    lmax = 1536
+    gen = torch.Generator().manual_seed(77)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    k, v = make_kv(B, Hkv, lmax, d, gen, poison_from=lens)
+    kp, vp, table = to_pages(k, v, bs, gen)
+    num_pages = kp.shape[0]
+    missing = {0: [3, 10, 23], 1: [0, 14]}
+    for b, js in missing.items():
+        for n, j in enumerate(js):
+            table[b, j] = -1 if n % 2 == 0 else num_pages + 7  # absent or out of the pool
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    nbm = dims.nb_max
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    # sparse: every block selected; the missing ones contribute nothing
+    idx = np.full((B, Hkv, nbm), -1, dtype=np.int32)
+    nsel = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        total = -(-lens[b] // bs)
+        idx[b, :, :total] = np.arange(total)
+        nsel[b] = total
+    ns = S.seer_decode_num_split(dims, nbm, 0)
+    ws = torch.zeros(S.seer_decode_workspace_bytes(dims, nbm, ns) // 4 + 64, dtype=torch.float32,
+                     device=DEV)
+    outs, lses = [], []
+    for dense in (False, True):
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+        if dense:
+            S.seer_dense_decode_paged(dims, q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), seq,
+                                      scale, ns, ws, out, lse)
+        else:
+            S.seer_sparse_decode_paged(dims, q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), seq,
+                                       torch.from_numpy(idx).to(DEV),
+                                       torch.from_numpy(nsel).to(DEV), nbm, scale, ns, ws, out,
+                                       lse)
+        outs.append(out)
+        lses.append(lse)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for b in range(B):
+        total = -(-lens[b] // bs)
+        present = [j for j in range(total) if j not in missing[b]]
+        for h in range(Hkv):
+            qq = f64(q[b, h * g:(h + 1) * g])
+            o_ref, l_ref = O.sparse_decode_pair(qq, f64(k[b, h, :lens[b]]), f64(v[b, h, :lens[b]]),
+                                                lens[b], present, bs, scale)
+            for out, lse, what in zip(outs, lses, ("sparse", "dense")):
+                assert_out_close(f64(out[b, h * g:(h + 1) * g]), o_ref, f"{what} b={b} h={h}")
+                assert_lse_close(f64(lse[b, h * g:(h + 1) * g]), l_ref, f"{what} b={b} h={h}")
+
+
+def test_paged_binding_rejects_bad_layout(S):
+    say("paged binding checks")
+    B, Hq, Hkv, d, bs, lmax = 1, 4, 1, 64, 64, 256
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    q = torch.zeros((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    kp = torch.zeros((4, Hkv, bs, d), dtype=torch.bfloat16, device=DEV)
+    table = torch.zeros((B, 4), dtype=torch.int32, device=DEV)
+    seq = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(1 << 16, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):  # page rows of the wrong length
+        S.seer_dense_decode_paged(dims, q, kp[..., :32].contiguous(), kp, table, seq, 0.1, 1, ws,
+                                  out)
+    with pytest.raises(TypeError):  # table of the wrong dtype
+        S.seer_dense_decode_paged(dims, q, kp, kp, table.to(torch.int64), seq, 0.1, 1, ws, out)
+    S.seer_dense_decode_paged(dims, q, kp, kp, table, seq, 0.1, 1, ws, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
 # ------------------------------------------------------ compression cache
 
 @pytest.mark.parametrize("d,dg,bs,lens", [(64, 64, 64, [1024, 70]), (128, 128, 64, [4100, 64]),
