@@ -33,7 +33,8 @@ __all__ = [
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
-    "seer_dense_decode_paged", "seer_decode_step_workspace_bytes",
+    "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
+    "seer_decode_step_workspace_bytes",
     "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
     "DecodeStep",
 ]
@@ -50,7 +51,8 @@ EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
     "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
-    "seer_dense_decode_paged", "seer_decode_step_workspace_bytes",
+    "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
+    "seer_decode_step_workspace_bytes",
     "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
 )
 
@@ -106,6 +108,9 @@ _SIGS = {
     "seer_dense_decode_paged": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, ctypes.c_int64,
                                        ctypes.c_int64, _I32, _P, _I32, _P, ctypes.c_float, _I32,
                                        _P, ctypes.c_size_t, _P, _P, _P]),
+    "seer_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SeerDims)]),
+    "seer_prefill_attention": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, ctypes.c_float, _P,
+                                      ctypes.c_size_t, _P, _P, _P, _P]),
     "seer_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SeerDims), _I32, _I32]),
     "seer_decode_step": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _I32, ctypes.c_double, _I32, _I32, ctypes.c_float, _I32, _P, _P,
@@ -343,6 +348,31 @@ def seer_dense_decode_paged(dims: SeerDims, q, k_pages, v_pages, block_table, se
         ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages), ps, phs, npg, _ptr(block_table),
         ts, _ptr(seq_lens), float(scale), int(num_split), wp, wn, _ptr(out), _ptr(lse), _stream(q)),
         "seer_dense_decode_paged")
+
+
+def seer_prefill_workspace_bytes(dims: SeerDims) -> int:
+    return int(lib().seer_prefill_workspace_bytes(ctypes.byref(dims)))
+
+
+def seer_prefill_attention(dims: SeerDims, q, k, v, seq_lens, scale: float, workspace, out, lse,
+                           gt=None) -> None:
+    """Causal prefill of whole sequences: q, out [B, H_q, Lmax, d] bf16, k, v
+    the [B, H_kv, Lmax, d] caches of `dims`, lse [B, H_q, Lmax] float32, gt
+    [B, H_kv, Lmax, NBmax] float32 or None."""
+    B, Hq, Hkv, d, L = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim, dims.max_seq_len
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, Hq, L, d), dev)
+    _check_kv(dims, k, "k")
+    _check_kv(dims, v, "v")
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    _need(out, "out", torch.bfloat16, (B, Hq, L, d), dev)
+    _need(lse, "lse", torch.float32, (B, Hq, L), dev)
+    if gt is not None:
+        _need(gt, "gt", torch.float32, (B, Hkv, L, dims.nb_max), dev)
+    wp, wn = _ws(workspace, dev)
+    _check(lib().seer_prefill_attention(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(seq_lens), float(scale), wp, wn, _ptr(out), _ptr(lse),
+                                        _ptr(gt), _stream(q)), "seer_prefill_attention")
 
 
 def seer_decode_step_workspace_bytes(dims: SeerDims, max_selected: int, num_split: int = 0) -> int:

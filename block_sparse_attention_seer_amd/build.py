@@ -25,7 +25,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libseer.so")
 
 SOURCES = ["seer_checks.cpp", "seer_api.cpp", "seer_runtime.cpp",
-           "decode.hip", "gate.hip", "select.hip"]
+           "decode.hip", "gate.hip", "select.hip", "prefill.hip"]
 
 ARCH = "gfx950"
 

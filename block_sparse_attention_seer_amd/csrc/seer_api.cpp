@@ -401,6 +401,32 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
                        inline_new > 0 ? kcomp_lens : nullptr, inline_new);
 }
 
+size_t seer_prefill_workspace_bytes(const seer_dims* dims) {
+  std::string why;
+  if (check_dims(dims, &why) != SEER_OK) return 0;
+  return seer::prefill_workspace_bytes(dims);
+}
+
+int seer_prefill_attention(const seer_dims* dims, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const int32_t* seq_lens, float scale,
+                           void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                           float* gt, void* stream) {
+  SEER_CHECK(check_dims(dims, &why_));
+  SEER_CHECK(check_ptr(q, 16, "q", &why_));
+  SEER_CHECK(check_ptr(k, 16, "k", &why_));
+  SEER_CHECK(check_ptr(v, 16, "v", &why_));
+  SEER_CHECK(check_ptr(seq_lens, 4, "seq_lens", &why_));
+  SEER_CHECK(check_ptr(out, 16, "out", &why_));
+  SEER_CHECK(check_ptr(lse, 4, "lse", &why_));
+  if (gt != nullptr) SEER_CHECK(check_ptr(gt, 4, "gt", &why_));
+  if (!std::isfinite(scale)) return fail(SEER_ERR_INVALID_ARG, "scale must be finite");
+  if (workspace == nullptr || workspace_bytes < seer::prefill_workspace_bytes(dims))
+    return fail(SEER_ERR_WORKSPACE, "prefill workspace missing or smaller than seer_prefill_workspace_bytes()");
+  SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
+  const seer::PrefillArgs a{q, k, v, seq_lens, scale, workspace, out, lse, gt};
+  return seer::launch_prefill(*dims, a, stream);
+}
+
 size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selected,
                                         int32_t num_split) {
   std::string why;

@@ -108,6 +108,23 @@ size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim)
   return counters + lse + parts * head_dim * sizeof(float);
 }
 
+int64_t prefill_padded_len(const seer_dims* d) {
+  return (static_cast<int64_t>(d->max_seq_len) + kPrefillTokenTile - 1) / kPrefillTokenTile *
+         kPrefillTokenTile;
+}
+
+size_t prefill_vt_bytes(const seer_dims* d) {
+  const size_t vt = static_cast<size_t>(d->batch) * d->num_kv_heads * d->head_dim *
+                    static_cast<size_t>(prefill_padded_len(d)) * 2;
+  return (vt + 255) / 256 * 256;
+}
+
+size_t prefill_workspace_bytes(const seer_dims* d) {
+  return prefill_vt_bytes(d) + static_cast<size_t>(d->batch) * d->num_q_heads *
+                                   static_cast<size_t>(nb_max(d)) *
+                                   static_cast<size_t>(prefill_padded_len(d)) * 4;
+}
+
 int auto_num_split(const seer_dims* d, int max_blocks, int num_cus) {
   // Measured on MI355X: the decode kernel keeps HBM busy once about eight
   // waves per compute unit are in flight chip-wide (each wave streams its

@@ -17,6 +17,7 @@ constexpr int kMaxSplit = 128;         // splits per (b, h) in the decode kernel
 constexpr int kDecodeMergeLds = 48 * 1024;  // LDS bytes for the decode wave merge
 constexpr int kMaxInlineNew = 4;       // new cache entries the gate launch computes itself
 constexpr int kCounterBytes = 256;     // alignment of the partial outputs after the partial lse
+constexpr int kPrefillTokenTile = 64;  // prefill: key tile, and the padding of the token axis
 
 // ------------------------------------------------------- argument checks
 // These live in a HIP-free translation unit so that a CPU-only test can
@@ -118,6 +119,26 @@ struct DecodeArgs {
   int64_t page_head_stride;
 };
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
+
+// Causal prefill attention with the fused ground truth (prefill.hip).
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq_lens;
+  float scale;
+  void* workspace;  // prefill_workspace_bytes(d)
+  uint16_t* out;
+  float* lse;
+  float* gt;        // or nullptr (attention only)
+};
+// Prefill workspace: V^T [B, H_kv, d, Lpad] bf16 (rounded up to 256 bytes),
+// then the row maxima [B, H_q, NBmax, Lpad] float32; Lpad = Lmax rounded
+// up to kPrefillTokenTile.
+int64_t prefill_padded_len(const seer_dims* d);
+size_t prefill_vt_bytes(const seer_dims* d);
+size_t prefill_workspace_bytes(const seer_dims* d);
+int launch_prefill(const seer_dims& d, const PrefillArgs& a, void* stream);
 
 // Waves per decode workgroup chosen automatically.
 // Waves per decode workgroup (8 or 4) and whether nw waves fit the LDS

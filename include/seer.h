@@ -12,6 +12,8 @@
  *   seer_kcomp_update  -> seer_gate_scores -> seer_select_blocks
  *   -> seer_sparse_decode            (seer_dense_decode is the full baseline)
  * or the same four stages fused into fewer launches by seer_decode_step.
+ * The training side has one call: seer_prefill_attention, the causal
+ * prefill forward with the gate's ground truth.
  *
  * Conventions shared by every call
  *   - "bf16" buffers hold raw bfloat16 bit patterns (uint16_t).
@@ -288,18 +290,18 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
                             void* stream);
 
 /*
- * seer_decode_step -- one whole decode step of one layer in three launches,
+ * seer_decode_step -- one whole decode step of one layer in two launches,
  * with the same results as seer_kcomp_update (with max_new_blocks), then
  * seer_gate_scores, seer_select_blocks and seer_sparse_decode, in that order
  * ([CP Knowl 5]: cache update, gating and binarisation; [CP Knowl 6]: the
  * block-sparse decode).
  *
- * Launch 1 forms the gate queries (one GEMM per KV head) and the cache
- * entries of blocks completed since the last update; launch 2 scores and
- * selects the blocks of each (b, h) in one workgroup, counting those new
- * entries; launch 3 is the sparse decode with its split merge, whose first
- * workgroup also raises kcomp_lens -- so kcomp_lens keeps its old value
- * until then and nothing else may read it in between.
+ * Launch 1 runs one workgroup per (b, h): the cache entries of blocks
+ * completed since the last update (up to 4; with max_new_blocks > 4 a
+ * staged cache update runs before it), the gate query, the block scores and
+ * the selection.  Launch 2 is the sparse decode with its split merge, whose
+ * first workgroup also raises kcomp_lens -- so kcomp_lens keeps its old
+ * value until then and nothing else may read it in between.
  *
  *   q_nope, q        [B, H_q, d] pre-/post-RoPE queries (may alias).
  *   k_nope, k_cache, v_cache  caches (layout above; k_nope may alias k_cache).
@@ -327,6 +329,37 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
                      int32_t* block_idx, int32_t* num_selected, float* logits,
                      float scale, int32_t num_split, void* workspace,
                      size_t workspace_bytes, uint16_t* out, float* lse, void* stream);
+
+/*
+ * seer_prefill_attention -- causal prefill attention of whole sequences (a
+ * FlashAttention-2 forward) and, optionally, the block-level ground truth
+ * that the AttnGate is distilled towards ([CP Knowl 3]): the attention map
+ * max-pooled over keys in blocks of b, max-pooled over the g query heads of
+ * each KV head, normalised to sum to 1 per query.  The ground truth is
+ * formed from each key tile's row maximum of the scores, stored during the
+ * forward and rescaled by the row's final max and normaliser afterwards
+ * ([CP Knowl 4]); the O(L^2) map is never built.
+ *
+ * The queries of sequence b are its tokens 0 .. L-1 (L = seq_lens[b],
+ * clamped to [0, Lmax]); query t attends keys 0 .. t.
+ *   q        [B, H_q, Lmax, d] bf16, contiguous.
+ *   k, v     [B, H_kv, Lmax, d] bf16 with the dims strides (as K, V above).
+ *   scale    softmax scale (1/sqrt(d)), finite.
+ *   workspace >= seer_prefill_workspace_bytes(dims) bytes, 256-byte aligned,
+ *            no initial contents needed: V transposed, then the stored row
+ *            maxima ([B, H_q, NBmax, Lmax rounded up to 64] float32).
+ *   out      [B, H_q, Lmax, d] bf16: attention output of rows t < L.
+ *   lse      [B, H_q, Lmax] float32: natural-log normaliser of rows t < L
+ *            (required).
+ *   gt       [B, H_kv, Lmax, NBmax] float32 ground truth of rows t < L
+ *            (blocks after the row's own are 0), or NULL for attention only.
+ * Rows t >= L of out, lse and gt are left untouched.  d, b and g as above.
+ */
+size_t seer_prefill_workspace_bytes(const seer_dims* dims);
+int seer_prefill_attention(const seer_dims* dims, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const int32_t* seq_lens, float scale,
+                           void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                           float* gt, void* stream);
 
 /* Host-only helpers. */
 const char* seer_status_string(int status);

@@ -19,6 +19,14 @@ Recipe (shared by every workload):
     tokens' attention logits by about 3 so that sparse and dense outputs
     differ measurably.  (The random gate does not know about them.)
   * Cache slots past a sequence's length are left as drawn (never read).
+
+Prefill workloads (the training-side forward with the gate's ground truth,
+whole sequences of up to 32k tokens as in the distillation):
+  * q, K, V ~ N(0, 1) in float32, rounded to bf16;
+  * each (sequence, KV head) has a random unit direction u shared by its
+    query heads: every query gets +4u, the key of token 0 gets +8u (an
+    attention sink) and the keys of `planted` random blocks get +8u, so the
+    attention map has the sink and a few heavy blocks instead of being flat.
 """
 
 from __future__ import annotations
@@ -97,6 +105,71 @@ WORKLOADS = {
                               topk_blocks=64, seq_len_range=(16384, 130816),
                               steps=256, seed=1005),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    max_seq_len: int
+    seq_lens: tuple           # one length per sequence
+    planted: int = 0          # heavy blocks per (sequence, KV head)
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def nb_max(self) -> int:
+        return -(-self.max_seq_len // self.block_size)
+
+
+PREFILL_WORKLOADS = {
+    "prefill_tiny": PrefillWorkload("prefill_tiny", batch=2, num_q_heads=4, num_kv_heads=2,
+                                    head_dim=64, block_size=64, max_seq_len=600,
+                                    seq_lens=(600, 333), planted=2, seed=2001),
+    # one Qwen3-14B-shaped attention layer over a 32k-token training sequence
+    "qwen3_14b_prefill_32k": PrefillWorkload("qwen3_14b_prefill_32k", batch=1, num_q_heads=40,
+                                             num_kv_heads=8, head_dim=128, block_size=64,
+                                             max_seq_len=32768, seq_lens=(32768,), planted=8,
+                                             seed=2002),
+}
+
+
+def make_prefill_inputs(w: PrefillWorkload, device: str = "cpu") -> dict:
+    """q [B, Hq, Lmax, d], k, v [B, Hkv, Lmax, d] bf16 and seq_lens [B] int32
+    on `device`, by the prefill recipe above."""
+    cpu_gen = torch.Generator(device="cpu").manual_seed(w.seed)
+    dev_gen = cpu_gen if device == "cpu" else torch.Generator(device=device).manual_seed(w.seed)
+    B, Hq, Hkv, d, L, bs = (w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_seq_len,
+                            w.block_size)
+    g = w.group
+    u = torch.randn((B, Hkv, d), generator=cpu_gen, dtype=torch.float32)
+    u = (u / u.norm(dim=-1, keepdim=True)).to(device)
+    q = torch.empty((B, Hq, L, d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((B, Hkv, L, d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, Hkv, L, d), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        for h in range(Hkv):
+            for i in range(g):
+                x = torch.randn((L, d), generator=dev_gen, device=device, dtype=torch.float32)
+                q[b, h * g + i] = (x + 4.0 * u[b, h]).to(torch.bfloat16)
+            x = torch.randn((L, d), generator=dev_gen, device=device, dtype=torch.float32)
+            x[0] += 8.0 * u[b, h]
+            nb = w.seq_lens[b] // bs
+            if nb > 1 and w.planted > 0:
+                for j in (torch.randperm(nb - 1, generator=cpu_gen)[:w.planted] + 1).tolist():
+                    x[j * bs:(j + 1) * bs] += 8.0 * u[b, h]
+            k[b, h] = x.to(torch.bfloat16)
+            v[b, h] = torch.randn((L, d), generator=dev_gen, device=device,
+                                  dtype=torch.float32).to(torch.bfloat16)
+    seq = torch.tensor(list(w.seq_lens), dtype=torch.int32, device=device)
+    return dict(q=q, k=k, v=v, seq_lens=seq)
 
 
 def draw_seq_lens(w: Workload, gen: torch.Generator) -> torch.Tensor:
