@@ -14,7 +14,11 @@ of the inputs (each step touches a different one).
 Prints one JSON line: µs per step (lower is better), achieved HBM bandwidth
 of the decode kernel on its algorithmic bytes against the 8 TB/s peak, the
 speedup over the library's own dense decode at equal shape, and the float64
-oracle timed on the host cores on a bounded sample.
+oracle timed on the host cores on a bounded sample.  The line also carries
+the training-side call, seer_prefill_attention (causal prefill forward with
+the gate's ground truth) on a 32k-token Qwen3-14B-shaped layer, against the
+2.5 PFLOP/s dense bf16 MFMA peak ("prefill_gt"; --prefill-only runs just
+that leg, for profiling).
 """
 
 from __future__ import annotations
@@ -33,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("sparse decode µs/step + achieved HBM GB/s (% peak); "
           "speedup vs dense @90% sparsity")
 PEAK_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRCS = [os.path.join(ROOT, "block_sparse_attention_seer_amd", "csrc", f)
                for f in ("decode.hip", "seer_device.hpp")]
@@ -76,6 +81,9 @@ def main() -> int:
     ap.add_argument("--num-split", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only seer_prefill_attention and print its object")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--traffic-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a few decode launches and a plain copy of "
                          "known size (the counters' scale), then exit")
@@ -101,6 +109,10 @@ def main() -> int:
     S.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.prefill_only:
+        print(json.dumps({"prefill_gt": prefill_leg(S, torch, dev, args.prefill_steps)}),
+              flush=True)
+        return 0
     w = WORKLOADS[args.workload]
     if w.seq_len is None:
         print("bench.py times single-length workloads (qwen3_8b_layer, qwen3_14b_b16, tiny)",
@@ -242,6 +254,9 @@ def main() -> int:
     if not args.no_cpu:
         cpu = cpu_baseline(reps[0][0], w, args.cpu_seconds)
 
+    log("prefill with ground truth")
+    prefill = prefill_leg(S, torch, dev, args.prefill_steps)
+
     traffic = measured_traffic()
     line = {
         "metric": METRIC,
@@ -286,9 +301,59 @@ def main() -> int:
         "kcomp_update_us_amortised": round(kcomp_us / bs, 3),
         "selected_fraction": round(sel_tokens / (B * Hkv * L), 4),
         "cpu_baseline": cpu,
+        "prefill_gt": prefill,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def prefill_leg(S, torch, dev, steps):
+    """seer_prefill_attention on the 32k-token Qwen3-14B-shaped layer: the
+    call with the ground truth and the attention-only call, each event-timed
+    over `steps` back-to-back calls on the launch stream.  `achieved` is the
+    algorithmic MFMA work (4 d flops per query-key pair the causal mask keeps:
+    2d for q.k, 2d for p.v) over the whole call, so the small V-transpose
+    and ground-truth kernels count against it."""
+    from workloads import PREFILL_WORKLOADS, make_prefill_inputs
+    w = PREFILL_WORKLOADS["qwen3_14b_prefill_32k"]
+    B, Hq, Hkv, d, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_seq_len
+    inp = make_prefill_inputs(w, device=str(dev))
+    dims = S.make_dims(B, Hq, Hkv, d, d, w.block_size, L)
+    ws = torch.empty(S.seer_prefill_workspace_bytes(dims) // 4 + 64, dtype=torch.float32,
+                     device=dev)
+    out = torch.empty((B, Hq, L, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    gt = torch.empty((B, Hkv, L, dims.nb_max), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    flops = sum(2.0 * d * n * (n + 1) for n in w.seq_lens) * Hq
+    us = {}
+    for label, g in (("gt", gt), ("attn", None)):
+        for _ in range(2):
+            S.seer_prefill_attention(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], scale,
+                                     ws, out, lse, g)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            S.seer_prefill_attention(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], scale,
+                                     ws, out, lse, g)
+        e1.record()
+        torch.cuda.synchronize()
+        us[label] = 1e3 * e0.elapsed_time(e1) / steps
+    achieved = flops / (us["gt"] * 1e-6) / 1e12
+    return {
+        "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+        "block_size": w.block_size, "seq_len": L, "calls": steps,
+        "us_per_call": round(us["gt"], 1),
+        "attention_only_us": round(us["attn"], 1),
+        "ground_truth_overhead": round(us["gt"] / us["attn"] - 1, 4),
+        "algorithmic_tflop": round(flops / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "seer_prefill_attention (vt_kernel + "
+                     "fa_fwd_kernel + gt_kernel)", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "attention_only_achieved": round(flops / (us["attn"] * 1e-6) / 1e12, 1)},
+    }
 
 
 def selected_tokens(st, L, bs):

@@ -239,22 +239,23 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(PrefillParams p) {
           sacc[mt] = mfma32(a, qop[ks], sacc[mt]);
         }
       }
-      // ---- scale, causal mask, tile row max
-      const bool diag = j * kKeys + kKeys - 1 > wfirst;
+      // ---- causal mask, tile row max (raw scores; the scale is positive,
+      // so scaling commutes with the max and goes into the exponent below)
+      if (j * kKeys + kKeys - 1 > wfirst) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j * kKeys + 32 * mt + 8 * (i / 4) + 4 * hf + (i % 4);
+            sacc[mt][i] = key > qrow ? -INFINITY : sacc[mt][i];
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s = sacc[mt][i] * p.scale_log2;
-          if (diag) {
-            const int key = j * kKeys + 32 * mt + 8 * (i / 4) + 4 * hf + (i % 4);
-            s = key > qrow ? -INFINITY : s;
-          }
-          sacc[mt][i] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mt][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
       if constexpr (GT) {
         if (BS == kKeys) {
           if (hf == 0 && qrow < L) rrow[static_cast<int64_t>(j) * p.Lpad] = tmax;
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(PrefillParams p) {
         float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          pv[i] = fast_exp2(sacc[mt][i] - mref);
+          pv[i] = fast_exp2(fmaf(sacc[mt][i], p.scale_log2, -mref));
           l_part += pv[i];
         }
 #pragma unroll

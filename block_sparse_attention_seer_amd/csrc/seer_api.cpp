@@ -419,7 +419,8 @@ int seer_prefill_attention(const seer_dims* dims, const uint16_t* q, const uint1
   SEER_CHECK(check_ptr(out, 16, "out", &why_));
   SEER_CHECK(check_ptr(lse, 4, "lse", &why_));
   if (gt != nullptr) SEER_CHECK(check_ptr(gt, 4, "gt", &why_));
-  if (!std::isfinite(scale)) return fail(SEER_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(SEER_ERR_INVALID_ARG, "scale must be finite and positive");
   if (workspace == nullptr || workspace_bytes < seer::prefill_workspace_bytes(dims))
     return fail(SEER_ERR_WORKSPACE, "prefill workspace missing or smaller than seer_prefill_workspace_bytes()");
   SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));

@@ -21,9 +21,13 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(uint16_t, b);
 }
-// Two floats -> packed bf16 pair (lo, hi).
+// Two floats -> packed bf16 pair (lo, hi), one v_cvt_pk_bf16_f32 (the same
+// rounding as f2bf on each).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }

@@ -344,7 +344,7 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
  * clamped to [0, Lmax]); query t attends keys 0 .. t.
  *   q        [B, H_q, Lmax, d] bf16, contiguous.
  *   k, v     [B, H_kv, Lmax, d] bf16 with the dims strides (as K, V above).
- *   scale    softmax scale (1/sqrt(d)), finite.
+ *   scale    softmax scale (1/sqrt(d)), finite and > 0.
  *   workspace >= seer_prefill_workspace_bytes(dims) bytes, 256-byte aligned,
  *            no initial contents needed: V transposed, then the stored row
  *            maxima ([B, H_q, NBmax, Lmax rounded up to 64] float32).
