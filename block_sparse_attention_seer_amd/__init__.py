@@ -438,7 +438,7 @@ class DecodeStep:
         self.block_idx = torch.empty((B, Hkv, self.max_selected), dtype=torch.int32, device=dev)
         self.num_selected = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         gws = seer_gate_workspace_bytes(dims)
-        self.gate_ws = torch.empty((max(gws, 16) // 4 + 4,), dtype=torch.float32, device=dev)
+        self.gate_ws = torch.zeros((max(gws, 16) // 4 + 4,), dtype=torch.float32, device=dev)
         self.num_split = seer_decode_num_split(dims, self.max_selected, num_split)
         dws = seer_decode_workspace_bytes(dims, self.max_selected, self.num_split)
         self.decode_ws = torch.zeros((max(dws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
