@@ -355,24 +355,13 @@ __global__ __launch_bounds__(256) void gt_kernel(PrefillParams p) {
   const float* rb = p.r + (static_cast<int64_t>(b) * p.Hq + hkv * G) * p.NBmax * p.Lpad + tok;
   const int64_t head_stride = static_cast<int64_t>(p.NBmax) * p.Lpad;
 
-  // ---- pass 1: row sums of the group maxima (fixed order: j by j within a
-  // thread, then the four threads of a row in order)
-  float sum = 0.f;
-  for (int j = jj; j < nvis; j += 4) {
-    float gm = 0.f;
-    for (int hg = 0; hg < G; ++hg)
-      gm = fmaxf(gm, fast_exp2(rb[hg * head_stride + static_cast<int64_t>(j) * p.Lpad] -
-                               s_lse[hg][t]));
-    sum += gm;
-  }
-  s_part[jj][t] = sum;
-  __syncthreads();
-  const float total = ((s_part[0][t] + s_part[1][t]) + s_part[2][t]) + s_part[3][t];
-  const float inv = total > 0.f ? 1.f / total : 0.f;
-
-  // ---- pass 2: normalised rows, 64 blocks at a time through LDS
+  // ---- pass 1: the group maxima, unnormalised, straight into the target
+  // rows (64 blocks at a time through LDS, coalesced stores), and their row
+  // sums (fixed order: j by j within a thread, then the four threads of a
+  // row in order).  r is read once.
   float* gtb = p.gt + (static_cast<int64_t>(pair) * p.Lmax + i0) * p.NBmax;
   const int rows = min(kRowTile, L - i0);
+  float sum = 0.f;
   for (int c0 = 0; c0 < p.NBmax; c0 += kRowTile) {
     if (c0 < nvis_max) {
       for (int m = jj; m < kRowTile; m += 4) {
@@ -382,7 +371,8 @@ __global__ __launch_bounds__(256) void gt_kernel(PrefillParams p) {
           for (int hg = 0; hg < G; ++hg)
             gm = fmaxf(gm, fast_exp2(rb[hg * head_stride + static_cast<int64_t>(j) * p.Lpad] -
                                      s_lse[hg][t]));
-        s_g[t][m] = gm * inv;
+        sum += gm;
+        s_g[t][m] = gm;
       }
     } else {
       for (int m = jj; m < kRowTile; m += 4) s_g[t][m] = 0.f;
@@ -394,6 +384,21 @@ __global__ __launch_bounds__(256) void gt_kernel(PrefillParams p) {
       if (col < cols) gtb[static_cast<int64_t>(row) * p.NBmax + c0 + col] = s_g[row][col];
     }
     __syncthreads();
+  }
+  s_part[jj][t] = sum;
+  __syncthreads();
+  if (threadIdx.x < kRowTile) {
+    const float total = ((s_part[0][t] + s_part[1][t]) + s_part[2][t]) + s_part[3][t];
+    s_lse[0][t] = total > 0.f ? 1.f / total : 0.f;  // reused: the row's 1/sum
+  }
+  __syncthreads();
+  // ---- pass 2: normalise the visible part of this workgroup's rows (just
+  // written by it, so read back from L2)
+  const int vis_cols = min(p.NBmax, nvis_max);
+  for (int i = threadIdx.x; i < rows * vis_cols; i += 256) {
+    const int row = i / vis_cols, col = i % vis_cols;
+    float* e = gtb + static_cast<int64_t>(row) * p.NBmax + col;
+    *e = *e * s_lse[0][row];
   }
 }
 
