@@ -31,7 +31,8 @@ __all__ = [
     "SeerError", "SeerDims", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "SELECT_TOPK", "SELECT_THRESHOLD", "SELECT_TOPP", "make_dims",
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
-    "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
+    "seer_select_blocks", "seer_decode_workspace_bytes", "seer_workspace_bytes",
+    "seer_decode_num_split",
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
     "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
     "seer_decode_step_workspace_bytes",
@@ -49,7 +50,8 @@ SELECT_TOPP = 3  # threshold carries the mass p
 
 EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
-    "seer_select_blocks", "seer_decode_workspace_bytes", "seer_decode_num_split",
+    "seer_select_blocks", "seer_decode_workspace_bytes", "seer_workspace_bytes",
+    "seer_decode_num_split",
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
     "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
     "seer_decode_step_workspace_bytes",
@@ -97,6 +99,7 @@ _SIGS = {
     "seer_select_blocks": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _I32, _I32, ctypes.c_float,
                                   _I32, _P, _P, _P]),
     "seer_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SeerDims), _I32, _I32]),
+    "seer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SeerDims), _I32, _I32]),
     "seer_decode_num_split": (_I32, [ctypes.POINTER(SeerDims), _I32, _I32, ctypes.POINTER(_I32)]),
     "seer_sparse_decode": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, _P, _P, _I32,
                                   ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
@@ -247,6 +250,10 @@ def seer_select_blocks(dims: SeerDims, logits, kcomp_lens, seq_lens, mode: int, 
                                     _ptr(seq_lens), int(mode), int(topk_blocks), float(threshold),
                                     int(max_selected), _ptr(block_idx), _ptr(num_selected),
                                     _stream(logits)), "seer_select_blocks")
+
+
+def seer_workspace_bytes(dims: SeerDims, max_blocks: int, num_split: int = 0) -> int:
+    return int(lib().seer_workspace_bytes(ctypes.byref(dims), int(max_blocks), int(num_split)))
 
 
 def seer_decode_workspace_bytes(dims: SeerDims, max_blocks: int, num_split: int = 0) -> int:

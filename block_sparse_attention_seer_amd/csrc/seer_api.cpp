@@ -179,6 +179,10 @@ size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks, in
                                       dims->head_dim);
 }
 
+size_t seer_workspace_bytes(const seer_dims* dims, int32_t max_blocks, int32_t num_split) {
+  return seer_decode_workspace_bytes(dims, max_blocks, num_split);
+}
+
 int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks, int32_t num_split,
                           int32_t* num_split_out) {
   SEER_CHECK(check_dims(dims, &why_));

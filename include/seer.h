@@ -201,6 +201,11 @@ int seer_select_blocks(const seer_dims* dims, const float* logits,
  */
 size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks,
                                    int32_t num_split);
+/* The same size under the name of the boundary's outline: bytes of the
+ * workspace of seer_sparse_decode / seer_dense_decode for max_blocks and
+ * num_split, exactly seer_decode_workspace_bytes(dims, max_blocks,
+ * num_split). */
+size_t seer_workspace_bytes(const seer_dims* dims, int32_t max_blocks, int32_t num_split);
 
 /* The split count a decode call will use (resolves num_split = 0). */
 int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks,

@@ -120,6 +120,7 @@ def test_host_only_sizes(S):
     assert S.seer_gate_workspace_bytes(d) == 16 * 8 * 128 * 4
     assert S.seer_decode_workspace_bytes(d, 53, 1) == 0
     assert S.seer_decode_workspace_bytes(d, 53, 4) == 512 + 10240 + 128 * 4 * 5 * 128 * 4
+    assert S.seer_workspace_bytes(d, 53, 4) == S.seer_decode_workspace_bytes(d, 53, 4)
 
 
 def test_checks_build_and_pass_under_host_sanitizers(tmp_path):
