@@ -392,6 +392,18 @@ def seer_decode_step(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w
                      topk_blocks: int, threshold: float, max_selected: int, block_idx,
                      num_selected, logits, scale: float, num_split: int, workspace, out,
                      lse=None) -> None:
+    args = _decode_step_args(dims, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                             kcomp_lens, kcomp, max_new_blocks, rope_theta, mode, topk_blocks,
+                             threshold, max_selected, block_idx, num_selected, logits, scale,
+                             num_split, workspace, out, lse)
+    _check(lib().seer_decode_step(*args, _stream(q)), "seer_decode_step")
+
+
+def _decode_step_args(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                      kcomp_lens, kcomp, max_new_blocks, rope_theta, mode, topk_blocks, threshold,
+                      max_selected, block_idx, num_selected, logits, scale, num_split, workspace,
+                      out, lse) -> tuple:
+    """Checks seer_decode_step's tensors; returns its arguments but the stream."""
     B, Hq, Hkv, d, dg = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim, dims.d_gate
     dev = q.device
     _check_decode_io(dims, q, k_cache, v_cache, seq_lens, out, lse)
@@ -406,12 +418,11 @@ def seer_decode_step(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w
     if logits is not None:  # optional: the selection reads the logits from LDS
         _need(logits, "logits", torch.float32, (B, Hkv, dims.nb_max), dev)
     wp, wn = _ws(workspace, dev)
-    _check(lib().seer_decode_step(
-        ctypes.byref(dims), _ptr(q_nope), _ptr(q), _ptr(k_nope), _ptr(k_cache), _ptr(v_cache),
-        _ptr(w_q), _ptr(w_k), _ptr(seq_lens), _ptr(kcomp_lens), _ptr(kcomp), int(max_new_blocks),
-        float(rope_theta), int(mode), int(topk_blocks), float(threshold), int(max_selected),
-        _ptr(block_idx), _ptr(num_selected), _ptr(logits), float(scale), int(num_split), wp, wn,
-        _ptr(out), _ptr(lse), _stream(q)), "seer_decode_step")
+    return (ctypes.byref(dims), _ptr(q_nope), _ptr(q), _ptr(k_nope), _ptr(k_cache), _ptr(v_cache),
+            _ptr(w_q), _ptr(w_k), _ptr(seq_lens), _ptr(kcomp_lens), _ptr(kcomp),
+            int(max_new_blocks), float(rope_theta), int(mode), int(topk_blocks), float(threshold),
+            int(max_selected), _ptr(block_idx), _ptr(num_selected), _ptr(logits), float(scale),
+            int(num_split), wp, wn, _ptr(out), _ptr(lse))
 
 
 class DecodeStep:
@@ -502,6 +513,36 @@ class DecodeStep:
             self.fused_step(q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens, scale,
                             max_new_blocks, keep_logits)
         return graph
+
+    def bind_step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                  scale: Optional[float] = None, max_new_blocks: int = 1,
+                  keep_logits: bool = False):
+        """Checks the fused step's tensors once and returns a callable that
+        issues the same seer_decode_step with them on the current stream.
+
+        For loops where the per-call checks of this binding would cost more
+        host time than the step's GPU work.  The tensors must stay alive and
+        in place (the callable holds them); their contents may change between
+        calls, as with ``capture_step``.
+        """
+        d = self.dims
+        if scale is None:
+            scale = 1.0 / math.sqrt(d.head_dim)
+        keep = (q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens)
+        args = _decode_step_args(d, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                                 self.kcomp_lens, self.kcomp, max_new_blocks, self.rope_theta,
+                                 self.mode, self.topk_blocks, self.threshold, self.max_selected,
+                                 self.block_idx, self.num_selected,
+                                 self.logits if keep_logits else None, scale, self.num_split,
+                                 self.step_ws, self.out, self.lse)
+        fn = lib().seer_decode_step
+        dev = q.device
+
+        def run() -> None:
+            _check(fn(*args, torch.cuda.current_stream(dev).cuda_stream), "seer_decode_step")
+
+        run.tensors = keep  # kept alive with the callable
+        return run
 
     def fused_step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
                    scale: Optional[float] = None, max_new_blocks: int = 1,

@@ -834,17 +834,22 @@ def test_pipeline_full_size_sampled(S):
 
 # ------------------------------------------------------------- graph capture
 
-def test_graph_replays_equal_eager_steps(S):
+@pytest.mark.parametrize("num_split", [0, 2])
+def test_graph_replays_equal_eager_steps(S, num_split):
     """A captured fused step, replayed after eager appends (some of which
     complete a block) with unrelated eager work in between, gives bit for bit
-    what the eager fused step gives on the same state, replay after replay."""
+    what the eager fused step gives on the same state, replay after replay,
+    with the automatic split and with two splits."""
     from workloads import append_token
     w = WORKLOADS["pipeline_128k"].replace(batch=4, max_seq_len=4096, seq_len_range=(700, 900))
     inp = make_inputs(w, device=DEV)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
-    eager = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
-    graphed = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
+    say(f"graph replay, split {num_split}")
+    eager = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks,
+                         num_split=num_split, device=DEV)
+    graphed = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks,
+                           num_split=num_split, device=DEV)
     eager.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
     _clone_state(eager, graphed)
     other = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
@@ -872,3 +877,49 @@ def test_graph_replays_equal_eager_steps(S):
             assert torch.equal(graphed.lse, eager.lse), step
     assert completed > 0  # some replays appended cache entries
     _check_pair(w, inp, graphed, 0, 0, "graph replay vs oracle")
+
+
+@pytest.mark.parametrize("num_split,mode", [(2, "topk"), (3, "threshold"), (4, "topp")])
+def test_bound_step_equals_staged(S, num_split, mode):
+    """The fused step at 2..4 splits in each selection mode, issued through
+    bind_step, equals the staged calls bit for bit over appends that
+    complete blocks (the step then raises kcomp_lens itself)."""
+    from workloads import append_token
+    tau = {"topk": 0.0, "threshold": 0.01, "topp": 0.9}[mode]
+    w = WORKLOADS["pipeline_128k"].replace(batch=3, max_seq_len=4096, seq_len_range=(1200, 1300),
+                                           mode=mode, tau=tau)
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    say(f"bound step split={num_split} mode={mode}")
+    kw = dict(mode=MODES[mode], topk_blocks=w.topk_blocks, threshold=tau, num_split=num_split,
+              device=DEV)
+    fused = S.DecodeStep(dims, **kw)
+    staged = S.DecodeStep(dims, **kw)
+    fused.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    _clone_state(fused, staged)
+    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+            inp["seq_lens"])
+    run = fused.bind_step(*args, keep_logits=True)
+    gen = torch.Generator(device=DEV).manual_seed(81)
+    completed = 0
+    for step in range(40):
+        before = inp["seq_lens"].clone()
+        append_token(inp, gen)
+        completed += int(((inp["seq_lens"] // 64) != (before // 64)).sum())
+        run()
+        staged.step(*args)
+        if step % 8 == 7 or step == 39:
+            torch.cuda.synchronize()
+            assert torch.equal(fused.kcomp_lens, staged.kcomp_lens), step
+            assert torch.equal(fused.kcomp, staged.kcomp), step
+            assert torch.equal(fused.num_selected, staged.num_selected), step
+            assert torch.equal(fused.block_idx, staged.block_idx), step
+            assert torch.equal(fused.logits, staged.logits), step
+            assert torch.equal(fused.out.view(torch.int16), staged.out.view(torch.int16)), step
+            assert torch.equal(fused.lse.view(torch.int32), staged.lse.view(torch.int32)), step
+    assert completed > 0
+    # the split counters at the start of the workspace are back at zero
+    pairs = w.batch * w.num_kv_heads
+    assert int(fused.step_ws.view(torch.int32)[:pairs].abs().sum()) == 0
+    _check_pair(w, inp, fused, 1, 3, "bound step vs oracle")
