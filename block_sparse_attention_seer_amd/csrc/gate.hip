@@ -6,7 +6,8 @@
 // block scores Q_gate K_gate^T / sqrt(d_gate).  [PN key design 1] (papernotes
 // page "Sparse Attention Adaptation for Long Reasoning"): one W_q per KV head.
 // [CP Knowl 5]: the K Compression Cache gets one entry per newly completed
-// block, once every b tokens; top-k or threshold then picks the blocks.
+// block, once every b tokens; top-k or threshold (or top-p, the adaptive
+// direction of [CP Knowl 14]) then picks the blocks.
 //
 // Kernels:
 //   prep_kernel    cache-entry tasks of the staged update: one newly

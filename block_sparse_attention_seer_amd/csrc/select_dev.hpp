@@ -25,6 +25,13 @@
 // below the interval's leading bit (8 bits per pass, so at most four).  If
 // the interval closes on one value, its duplicates are taken in index order
 // (lower index first).
+//
+// Top-p ([CP Knowl 14] names it as the adaptive direction) runs the same
+// narrowing with probability mass in place of counts: each key's softmax
+// mass is rounded to an integer number of 2^-30 units, the buckets sum those
+// integers, and the cut is the first key (descending, equal logits in index
+// order) where the running mass reaches ceil(p * 2^30) -- exact and
+// independent of the summation order.
 #pragma once
 
 #include "../../include/seer.h"
