@@ -195,6 +195,44 @@ def test_decode_is_deterministic(S):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_decode_workspace_partials_poisoned(S):
+    """The split partials in the workspace are always written before they
+    are read: with everything but the counters pre-filled with NaN, the
+    outputs equal a run on a zero-filled workspace bit for bit."""
+    say("decode with a NaN-poisoned workspace")
+    B, Hq, Hkv, d, bs, L = 3, 16, 4, 128, 64, 3000
+    gen = torch.Generator().manual_seed(23)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16).to(DEV)
+    k, v = make_kv(B, Hkv, L, d, gen)
+    k, v = k.to(DEV), v.to(DEV)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, L)
+    seq = torch.tensor([L, 1500, 65], dtype=torch.int32, device=DEV)
+    nbm = dims.nb_max
+    rng = np.random.default_rng(24)
+    idx, nsel = random_selection([L, 1500, 65], bs, Hkv, nbm, rng)
+    idx_d, nsel_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(nsel).to(DEV)
+    counter_words = -(-(B * Hkv * 4) // 256) * 256 // 4
+    for ns in (2, 3):
+        n = S.seer_decode_workspace_bytes(dims, nbm, ns) // 4 + 64
+        res = []
+        for poison in (False, True):
+            ws = torch.zeros(n, dtype=torch.float32, device=DEV)
+            if poison:
+                ws[counter_words:] = float("nan")
+            out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+            S.seer_sparse_decode(dims, q, k, v, seq, idx_d, nsel_d, nbm, 0.088, ns, ws, out, lse)
+            dout = torch.empty_like(out)
+            dlse = torch.empty_like(lse)
+            S.seer_dense_decode(dims, q, k, v, seq, 0.088, ns, ws, dout, dlse)
+            torch.cuda.synchronize()
+            res.append((out, lse, dout, dlse))
+        for a, b in zip(*res):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+        assert torch.isfinite(res[1][0].float()).all() and torch.isfinite(res[1][2].float()).all()
+
+
 def test_decode_strided_kv_layout(S):
     say("decode strided KV [B, L, H, d]")
     B, Hq, Hkv, d, bs, L = 2, 8, 2, 128, 64, 700
