@@ -81,6 +81,8 @@ def main() -> int:
     ap.add_argument("--num-split", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--flushed-iters", type=int, default=100,
+                    help="iterations of the per-iteration timing with a 1 GiB cache flush")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only seer_prefill_attention and print its object")
     ap.add_argument("--prefill-steps", type=int, default=5)
@@ -240,6 +242,41 @@ def main() -> int:
     dense_bytes = B * Hkv * L * 2 * d * 2 + qo_bytes
     dense_gbps = dense_bytes / (dense_us * 1e-6) / 1e9
 
+    # ---- per-iteration timing with the caches flushed: before each timed
+    # iteration 1 GiB goes through the memory system outside the timed region,
+    # so the 256 MB Infinity Cache and the L2s hold nothing of the step's data;
+    # each iteration is event-timed on its own (median, p10, p90).  Two
+    # flushes: writing 1 GiB, which leaves the Infinity Cache full of dirty
+    # lines whose write-back then shares HBM with the timed reads, and reading
+    # 1 GiB, which evicts as thoroughly without that write-back.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flushed(fn, iters, warm, how):
+        times = []
+        for i in range(warm + iters):
+            if how == "write":
+                flush.fill_(float(i))
+            else:
+                flush.sum()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            fn(i % R)
+            b_.record()
+            torch.cuda.synchronize()
+            if i >= warm:
+                times.append(a_.elapsed_time(b_) * 1e3)
+        q = np.percentile(times, [10, 50, 90])
+        return {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2),
+                "p90": round(float(q[2]), 2)}
+
+    log("flushed per-iteration timing")
+    flushed_step = {how + "_flush": flushed(step, args.flushed_iters, 10, how)
+                    for how in ("read", "write")}
+    flushed_decode = {how + "_flush": flushed(decode_only, args.flushed_iters, 10, how)
+                      for how in ("read", "write")}
+    flushed_dense = {"read_flush": flushed(dense, max(10, args.flushed_iters // 5), 3, "read")}
+    del flush
+
     # ---- amortised cost of a real cache update (one block per (b, h))
     inp0, st0 = reps[0]
     kupd = []
@@ -295,6 +332,11 @@ def main() -> int:
                       "elapsed / K",
         },
         "step_us_events": round(step_gpu_us, 3),
+        "step_us_flushed": flushed_step,
+        "decode_us_flushed": flushed_decode,
+        "dense_us_flushed": flushed_dense,
+        "speedup_vs_dense_step_read_flush": round(flushed_dense["read_flush"]["median"] /
+                                                  flushed_step["read_flush"]["median"], 3),
         "step_us_graph_replay": round(graph_us, 3),
         "step_algorithmic_bytes": int(step_alg),
         "step_GBps": round(step_gbps, 1),
