@@ -261,7 +261,12 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   const uint16_t* xq =
       p.q_nope + (static_cast<int64_t>(b) * p.Hq + h * p.G) * D + 32 * (n >> 2) + 8 * g;
   uint4 wb[TQ][kQueryChunks], xa[kQueryChunks];
-  load_query_group<TQ>(wb, xa, wq, xq, 0, nch, K, n, g, w);
+  // The 16 workgroups of a KV head share its W_q rows and run on one XCD
+  // (workgroups go round-robin over the 8 XCDs); each sequence starts its
+  // waves at a different row group so that they do not all request the
+  // same L2 lines at once.  Each row's arithmetic is unchanged.
+  const int wr = (w + b) & (kGateThreads / 64 - 1);
+  load_query_group<TQ>(wb, xa, wq, xq, 0, nch, K, n, g, wr);
 
   const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 32 * n + 8 * g;
   const int passes = max(1, (nc + kGateRows - 1) / kGateRows);
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
 #pragma unroll
     for (int t = 0; t < TQ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < nch; c0 += kQueryChunks) {
-      if (c0 > 0) load_query_group<TQ>(wb, xa, wq, xq, c0, nch, K, n, g, w);
+      if (c0 > 0) load_query_group<TQ>(wb, xa, wq, xq, c0, nch, K, n, g, wr);
 #pragma unroll
       for (int c = 0; c < kQueryChunks; ++c)
 #pragma unroll
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
     }
     if (g == (n & 3)) {
 #pragma unroll
-      for (int t = 0; t < TQ; ++t) s_part[(w * TQ + t) * 4 + (n >> 2)][g] = acc[t][0];
+      for (int t = 0; t < TQ; ++t) s_part[(wr * TQ + t) * 4 + (n >> 2)][g] = acc[t][0];
     }
   }
   __syncthreads();
