@@ -82,7 +82,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flushed-iters", type=int, default=100,
-                    help="iterations of the per-iteration timing with a 1 GiB cache flush")
+                    help="iterations of the per-iteration timing with a 1 GiB cache flush "
+                         "(0 skips it)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only seer_prefill_attention and print its object")
     ap.add_argument("--prefill-steps", type=int, default=5)
@@ -269,12 +270,15 @@ def main() -> int:
         return {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2),
                 "p90": round(float(q[2]), 2)}
 
-    log("flushed per-iteration timing")
-    flushed_step = {how + "_flush": flushed(step, args.flushed_iters, 10, how)
-                    for how in ("read", "write")}
-    flushed_decode = {how + "_flush": flushed(decode_only, args.flushed_iters, 10, how)
-                      for how in ("read", "write")}
-    flushed_dense = {"read_flush": flushed(dense, max(10, args.flushed_iters // 5), 3, "read")}
+    flushed_step = flushed_decode = flushed_dense = None
+    if args.flushed_iters > 0:  # 0: skipped (profiler runs)
+        log("flushed per-iteration timing")
+        flushed_step = {how + "_flush": flushed(step, args.flushed_iters, 10, how)
+                        for how in ("read", "write")}
+        flushed_decode = {how + "_flush": flushed(decode_only, args.flushed_iters, 10, how)
+                          for how in ("read", "write")}
+        flushed_dense = {"read_flush": flushed(dense, max(10, args.flushed_iters // 5), 3,
+                                               "read")}
     del flush
 
     # ---- amortised cost of a real cache update (one block per (b, h))
@@ -335,8 +339,9 @@ def main() -> int:
         "step_us_flushed": flushed_step,
         "decode_us_flushed": flushed_decode,
         "dense_us_flushed": flushed_dense,
-        "speedup_vs_dense_step_read_flush": round(flushed_dense["read_flush"]["median"] /
-                                                  flushed_step["read_flush"]["median"], 3),
+        "speedup_vs_dense_step_read_flush": (
+            round(flushed_dense["read_flush"]["median"] / flushed_step["read_flush"]["median"], 3)
+            if flushed_step is not None else None),
         "step_us_graph_replay": round(graph_us, 3),
         "step_algorithmic_bytes": int(step_alg),
         "step_GBps": round(step_gbps, 1),

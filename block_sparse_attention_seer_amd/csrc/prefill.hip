@@ -227,18 +227,22 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(PrefillParams p) {
       const uint16_t* sk = s_k[buf];
       const uint16_t* sv = s_v[buf];
       // ---- S^T for keys 64 j + 32 mt + (8(i/4) + 4 hf + i%4), query ln
+      // (both contractions alternate their independent accumulators, so no
+      // MFMA waits on the one just issued; each accumulator still takes its
+      // k-steps in order)
       f32x16_t sacc[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
           const uint4 a = *reinterpret_cast<const uint4*>(sk + (32 * mt + ln) * KROW + 16 * ks +
                                                           8 * hf);
           sacc[mt] = mfma32(a, qop[ks], sacc[mt]);
         }
-      }
       // ---- causal mask, tile row max (raw scores; the scale is positive,
       // so scaling commutes with the max and goes into the exponent below)
       if (j * kKeys + kKeys - 1 > wfirst) {
@@ -297,9 +301,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(PrefillParams p) {
       }
       // ---- O^T += V^T P^T (keys in the stored quad order of vt_kernel)
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int t = 0; t < DT; ++t) {
           const uint4 a = *reinterpret_cast<const uint4*>(sv + (32 * t + ln) * VROW + 16 * ks +
                                                           8 * hf);
           oacc[t] = mfma32(a, pb[ks], oacc[t]);
