@@ -366,17 +366,33 @@ __global__ __launch_bounds__(256) void gt_kernel(PrefillParams p) {
   float* gtb = p.gt + (static_cast<int64_t>(pair) * p.Lmax + i0) * p.NBmax;
   const int rows = min(kRowTile, L - i0);
   float sum = 0.f;
+  constexpr int MPT = kRowTile / 4;  // blocks of a 64-block chunk per thread
   for (int c0 = 0; c0 < p.NBmax; c0 += kRowTile) {
     if (c0 < nvis_max) {
-      for (int m = jj; m < kRowTile; m += 4) {
-        const int j = c0 + m;
-        float gm = 0.f;
-        if (j < nvis)
-          for (int hg = 0; hg < G; ++hg)
-            gm = fmaxf(gm, fast_exp2(rb[hg * head_stride + static_cast<int64_t>(j) * p.Lpad] -
-                                     s_lse[hg][t]));
-        sum += gm;
-        s_g[t][m] = gm;
+      // head by head, the MPT loads of a head are independent and issued
+      // together (indices clamped into the buffer; blocks after the query
+      // are masked to 0 below)
+      float gm[MPT];
+#pragma unroll
+      for (int mi = 0; mi < MPT; ++mi) gm[mi] = 0.f;
+      for (int hg = 0; hg < G; ++hg) {
+        const float* rh = rb + hg * head_stride;
+        const float lh = s_lse[hg][t];
+        float x[MPT];
+#pragma unroll
+        for (int mi = 0; mi < MPT; ++mi) {
+          const int j = min(c0 + jj + 4 * mi, p.NBmax - 1);
+          x[mi] = rh[static_cast<int64_t>(j) * p.Lpad];
+        }
+#pragma unroll
+        for (int mi = 0; mi < MPT; ++mi) gm[mi] = fmaxf(gm[mi], fast_exp2(x[mi] - lh));
+      }
+#pragma unroll
+      for (int mi = 0; mi < MPT; ++mi) {
+        const int m = jj + 4 * mi;
+        const float v = (c0 + m < nvis) ? gm[mi] : 0.f;
+        sum += v;
+        s_g[t][m] = v;
       }
     } else {
       for (int m = jj; m < kRowTile; m += 4) s_g[t][m] = 0.f;
