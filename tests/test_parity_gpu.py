@@ -836,6 +836,45 @@ def test_fused_step_full_size_sampled(S, name, pairs):
     torch.cuda.empty_cache()
 
 
+def test_fused_step_threshold_full_size_sampled(S):
+    """The 64-sequence threshold workload (b = 128, lengths never a multiple
+    of b, so every pair has a forced partial block) through the fused step
+    with the automatic split: sampled pairs against the oracle, every count
+    within the capacity, and each row's partial block present."""
+    w = WORKLOADS["threshold_b128"]
+    say("fused full size threshold_b128: generating inputs")
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    st = S.DecodeStep(dims, mode=S.SELECT_THRESHOLD, threshold=w.tau, device=DEV)
+    seq = inp["seq_lens"]
+    st.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq,
+                  keep_logits=False)
+    torch.cuda.synchronize()
+    say("fused full size threshold_b128: checking")
+    lens = seq.cpu().tolist()
+    assert st.kcomp_lens.cpu().tolist() == [int(L) // w.block_size for L in lens]
+    nsel = st.num_selected.cpu()
+    idx = st.block_idx.cpu()
+    assert bool(((nsel >= 1) & (nsel <= st.max_selected)).all())
+    for b, L in enumerate(lens):
+        last = -(-int(L) // w.block_size) - 1  # the partial block, always selected
+        for h in range(w.num_kv_heads):
+            n = int(nsel[b, h])
+            row = idx[b, h, :n]
+            assert int(row[-1]) == last and bool((row[1:] > row[:-1]).all())
+            assert bool((idx[b, h, n:] == -1).all())
+    all_pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    rng = np.random.default_rng(3)
+    for i in rng.choice(len(all_pairs), size=8, replace=False):
+        b, h = all_pairs[i]
+        _check_pair(w, inp, st, b, h, f"fused threshold b={b} h={h}")
+    assert torch.isfinite(st.out.float()).all() and torch.isfinite(st.lse).all()
+    del inp
+    torch.cuda.empty_cache()
+
+
 def test_pipeline_full_size_sampled(S):
     """The 128k pipeline workload at full size (32 sequences, lengths up to
     131072): bulk cache build, then fused steps with appends, checking sampled
