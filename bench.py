@@ -87,6 +87,11 @@ def main() -> int:
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only seer_prefill_attention and print its object")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--extra", action="store_true",
+                    help="instead of the headline line: one JSON line each for the Qwen3-8B-shaped "
+                         "layer, the 64-sequence threshold batch, the 256-step 128k pipeline and "
+                         "the pages' microbenchmark grid (64/8 heads, batch 1/4/16, 8k/32k/128k, "
+                         "50%%/90%% sparsity)")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a few decode launches and a plain copy of "
                          "known size (the counters' scale), then exit")
@@ -116,6 +121,8 @@ def main() -> int:
         print(json.dumps({"prefill_gt": prefill_leg(S, torch, dev, args.prefill_steps)}),
               flush=True)
         return 0
+    if args.extra:
+        return extra_lines(S, torch, np, dev)
     w = WORKLOADS[args.workload]
     if w.seq_len is None:
         print("bench.py times single-length workloads (qwen3_8b_layer, qwen3_14b_b16, tiny)",
@@ -496,6 +503,212 @@ def cpu_baseline(inp, w, budget_s):
                       f"{len(pairs)}; median pair time x {len(pairs)} pairs; NumPy float64, "
                       f"BLAS threads at default"}
 
+
+
+# ----------------------------------------------------------------- --extra
+
+
+def _events_us(torch, fn, n):
+    """Average µs of n back-to-back calls fn(i), one event pair around them."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / n
+
+
+def _flushed_median_us(torch, fn, n, flush):
+    """Median µs of n calls, each event-timed on its own after 1 GiB has been
+    read outside the timed region (cold Infinity Cache and L2)."""
+    times = []
+    for i in range(n + 3):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(1e3 * a.elapsed_time(b))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def _dense_buffers(S, torch, dims, dev):
+    """Split count, zeroed workspace and outputs of a dense decode call."""
+    ns = S.seer_decode_num_split(dims, dims.nb_max, 0)
+    ws = torch.zeros(max(S.seer_decode_workspace_bytes(dims, dims.nb_max, ns), 256) // 4 + 64,
+                     dtype=torch.float32, device=dev)
+    out = torch.empty((dims.batch, dims.num_q_heads, dims.head_dim), dtype=torch.bfloat16,
+                      device=dev)
+    lse = torch.empty((dims.batch, dims.num_q_heads), dtype=torch.float32, device=dev)
+    return ns, ws, out, lse
+
+
+def _selected_tokens(st, lens, bs):
+    ns = st.num_selected.cpu().numpy()
+    idx = st.block_idx.cpu().numpy()
+    tot = 0
+    for b_ in range(ns.shape[0]):
+        L = int(lens[b_])
+        for h_ in range(ns.shape[1]):
+            for j in idx[b_, h_, :ns[b_, h_]]:
+                tot += max(0, min(bs, L - int(j) * bs))
+    return tot
+
+
+def extra_lines(S, torch, np, dev):
+    """Measurements beyond the headline configuration, one JSON line each."""
+    from workloads import WORKLOADS, make_inputs
+    modes = {"topk": S.SELECT_TOPK, "threshold": S.SELECT_THRESHOLD}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    # ---- single steps of the Qwen3-8B-shaped layer and the threshold batch
+    for name in ("qwen3_8b_layer", "threshold_b128"):
+        w = WORKLOADS[name]
+        log(f"extra: {name}")
+        B, Hq, Hkv, d, dg, bs = (w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                                 w.block_size)
+        dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
+        scale = 1.0 / math.sqrt(d)
+        reps = []
+        for r in range(2):
+            inp = make_inputs(w.replace(seed=w.seed + 7919 * r), device=str(dev))
+            st = S.DecodeStep(dims, mode=modes[w.mode], topk_blocks=w.topk_blocks,
+                              threshold=w.tau, device=dev)
+            st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+            run = st.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                               inp["w_k"], inp["seq_lens"], scale, 1, False)
+            reps.append((inp, st, run))
+        for i in range(10):
+            reps[i % 2][2]()
+        step_us = _events_us(torch, lambda i: reps[i % 2][2](), 100)
+
+        def dec(i):
+            inp, st, _ = reps[i % 2]
+            S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"],
+                                 st.block_idx, st.num_selected, st.max_selected, scale,
+                                 st.num_split, st.decode_ws, st.out, st.lse)
+
+        dn = _dense_buffers(S, torch, dims, dev)
+
+        def dense(i):
+            inp = reps[i % 2][0]
+            S.seer_dense_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], scale, *dn)
+
+        dec_us = _events_us(torch, dec, 100)
+        dense_us = _events_us(torch, dense, 10)
+        lens = reps[0][0]["seq_lens"].cpu().numpy()
+        sel = float(np.mean([_selected_tokens(st, inp["seq_lens"].cpu().numpy(), bs)
+                             for inp, st, _ in reps]))
+        qo = 2 * B * Hq * d * 2
+        idx_bytes = B * Hkv * (reps[0][1].max_selected + 1) * 4
+        dec_alg = sel * 2 * d * 2 + qo + idx_bytes
+        step_alg = dec_alg + sum(int(L) // bs for L in lens) * Hkv * dg * 2 + Hkv * dg * (Hq // Hkv) * d * 2
+        dense_bytes = int(lens.sum()) * Hkv * 2 * d * 2 + qo
+        print(json.dumps({
+            "kind": "config", "workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+            "head_dim": d, "block_size": bs, "mode": w.mode,
+            "seq_len": int(lens[0]) if w.seq_len else [int(lens.min()), int(lens.max())],
+            "step_us": round(step_us, 2), "decode_us": round(dec_us, 2),
+            "decode_GBps": round(dec_alg / (dec_us * 1e-6) / 1e9, 1),
+            "decode_frac_of_peak": round(dec_alg / (dec_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+            "step_GBps": round(step_alg / (step_us * 1e-6) / 1e9, 1),
+            "dense_us": round(dense_us, 2),
+            "dense_GBps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+            "speedup_vs_dense_step": round(dense_us / step_us, 3),
+            "speedup_vs_dense_kernel": round(dense_us / dec_us, 3),
+            "selected_fraction": round(sel / float(lens.sum() * Hkv), 4),
+            "timing": "event pair around back-to-back launches, two input replicas alternating",
+        }), flush=True)
+        del reps
+        torch.cuda.empty_cache()
+
+    # ---- the 256-step pipeline: appends, block completions, fused steps
+    w = WORKLOADS["pipeline_128k"]
+    log("extra: pipeline_128k")
+    B, Hq, Hkv, d, dg, bs = (w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                             w.block_size)
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
+    scale = 1.0 / math.sqrt(d)
+    inp = make_inputs(w, device=str(dev))  # the appended tokens' K/V are drawn up front
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=dev)
+    L0 = inp["seq_lens"].clone()
+    lens = [(L0 + s + 1).to(torch.int32) for s in range(w.steps)]
+    runs = [st.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                         inp["w_k"], lens[s], scale, 1, False) for s in range(w.steps)]
+    times = []
+    for rep in range(2):  # the first pass warms up; the second is timed
+        st.build_cache(inp["k"], inp["w_k"], L0)
+        torch.cuda.synchronize()
+        times.append(_events_us(torch, lambda i: runs[i](), w.steps))
+    l0 = L0.cpu().numpy().astype(np.int64)
+    completions = int(((l0 + w.steps) // bs - l0 // bs).sum())
+    dn = _dense_buffers(S, torch, dims, dev)
+    dense_last = _events_us(torch, lambda i: S.seer_dense_decode(
+        dims, inp["q"], inp["k"], inp["v"], lens[-1], scale, *dn), 5)
+    print(json.dumps({
+        "kind": "pipeline", "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+        "head_dim": d, "block_size": bs, "topk_blocks": w.topk_blocks, "steps": w.steps,
+        "start_len": [int(l0.min()), int(l0.max())],
+        "us_per_step": round(times[1], 2), "block_completions": completions,
+        "dense_us_at_last_length": round(dense_last, 2),
+        "speedup_vs_dense_step": round(dense_last / times[1], 3),
+        "timing": "event pair around the 256 fused steps (cache update, gate, selection, "
+                  "decode), after one untimed pass from the same start",
+    }), flush=True)
+    del inp, st, runs
+    torch.cuda.empty_cache()
+
+    # ---- the pages' microbenchmark grid: kernel-level sparse vs dense
+    base = WORKLOADS["qwen3_8b_layer"]
+    for B in (1, 4, 16):
+        for L in (8192, 32768, 131072):
+            wgrid = base.replace(name="grid", batch=B, num_q_heads=64, num_kv_heads=8,
+                                 seq_len=L, max_seq_len=L, seed=3000 + B + L)
+            log(f"extra: grid batch {B} length {L}")
+            inp = make_inputs(wgrid, device=str(dev))
+            dims = S.make_dims(B, 64, 8, 128, 128, 64, L)
+            nb = L // 64
+            for sp in (0.5, 0.9):
+                k = math.ceil((1 - sp) * nb)
+                st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=k, device=dev)
+                st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+                st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                              inp["w_k"], inp["seq_lens"], keep_logits=False)
+                dn = _dense_buffers(S, torch, dims, dev)
+                torch.cuda.synchronize()
+                scale = 1.0 / math.sqrt(128)
+
+                def dec(i):
+                    S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"],
+                                         st.block_idx, st.num_selected, st.max_selected, scale,
+                                         st.num_split, st.decode_ws, st.out, st.lse)
+
+                def dense(i):
+                    S.seer_dense_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"],
+                                        scale, *dn)
+
+                sp_us = _flushed_median_us(torch, dec, 30, flush)
+                de_us = _flushed_median_us(torch, dense, 10, flush)
+                sel = _selected_tokens(st, inp["seq_lens"].cpu().numpy(), 64)
+                alg = sel * 2 * 128 * 2 + 2 * B * 64 * 128 * 2 + B * 8 * (st.max_selected + 1) * 4
+                print(json.dumps({
+                    "kind": "grid", "batch": B, "q_heads": 64, "kv_heads": 8, "head_dim": 128,
+                    "block_size": 64, "seq_len": L, "sparsity": sp, "topk_blocks": k,
+                    "sparse_decode_us": round(sp_us, 2), "dense_decode_us": round(de_us, 2),
+                    "speedup_kernel": round(de_us / sp_us, 3),
+                    "sparse_GBps": round(alg / (sp_us * 1e-6) / 1e9, 1),
+                    "timing": "median of per-launch event pairs, 1 GiB read before each",
+                }), flush=True)
+                del st
+            del inp
+            torch.cuda.empty_cache()
+    del flush
+    return 0
 
 if __name__ == "__main__":
     sys.exit(main())
