@@ -293,6 +293,55 @@ def random_selection(lens, bs, Hkv, max_sel, rng):
     return idx, nsel
 
 
+def test_sparse_decode_long_index_row_matches_oracle(S):
+    """Selections longer than the kernel's LDS copy of the index row (512
+    entries): entries past it are read from HBM.  Every pair against the
+    oracle, with one split and with the automatic split."""
+    say("sparse decode with index rows longer than the LDS copy")
+    d, bs, Hq, Hkv = 128, 64, 8, 2
+    lens = [40000, 35000]
+    B, g = len(lens), Hq // Hkv
+    lmax = max(lens) + 5
+    gen = torch.Generator().manual_seed(97)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    k, v = make_kv(B, Hkv, lmax, d, gen, poison_from=lens)
+    max_sel = 600  # <= NBmax = 626
+    rng = np.random.default_rng(98)
+    idx = np.full((B, Hkv, max_sel), -1, dtype=np.int32)
+    nsel = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        total = -(-lens[b] // bs)
+        for h in range(Hkv):
+            n = int(rng.integers(520, min(total, max_sel) + 1))  # always past entry 512
+            chosen = sorted(rng.choice(total, size=n, replace=False).tolist())
+            idx[b, h, :n] = chosen
+            nsel[b, h] = n
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    idx_d, nsel_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(nsel).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    for num_split in (1, 0):
+        ns = S.seer_decode_num_split(dims, max_sel, num_split)
+        ws = torch.zeros(max(S.seer_decode_workspace_bytes(dims, max_sel, ns), 4) // 4 + 64,
+                         dtype=torch.float32, device=DEV)
+        out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        S.seer_sparse_decode(dims, qd, kd, vd, seq, idx_d, nsel_d, max_sel, scale, num_split, ws,
+                             out, lse)
+        torch.cuda.synchronize()
+        og, lg = f64(out), f64(lse)
+        for b in range(B):
+            for h in range(Hkv):
+                qq = f64(q[b, h * g:(h + 1) * g])
+                kk, vv = f64(k[b, h, :lens[b]]), f64(v[b, h, :lens[b]])
+                blocks = idx[b, h, :nsel[b, h]].tolist()
+                o_ref, l_ref = O.sparse_decode_pair(qq, kk, vv, lens[b], blocks, bs, scale)
+                what = f"b={b} h={h} split={num_split}"
+                assert_out_close(og[b, h * g:(h + 1) * g], o_ref, what)
+                assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, what)
+
+
 PAGED_CASES = [
     # d, bs, Hq, Hkv, lens, table_pad
     (128, 64, 40, 8, [4096, 700, 1], 0),
