@@ -429,9 +429,12 @@ class DecodeStep:
     """Buffers and calls of one layer's decode step (allocation via torch).
 
     Holds the K Compression Cache (kcomp, kcomp_lens), the logits, the index
-    tensor and the two workspaces; ``step`` runs kcomp update, gate, select
-    and sparse decode on the current stream.  The decode workspace is
-    zero-filled once here, as the ABI requires.
+    tensor, the outputs and three workspaces (gate, decode, fused step).
+    ``step`` runs the staged calls (kcomp update, gate, select, sparse
+    decode) on the current stream; ``fused_step``, ``bind_step`` and
+    ``capture_step`` run the same step through seer_decode_step.  The
+    workspaces are zero-filled once here, as the ABI requires of the decode
+    counters.
     """
 
     def __init__(self, dims: SeerDims, *, mode: int, topk_blocks: int = 0, threshold: float = 0.0,
