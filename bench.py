@@ -586,6 +586,14 @@ def extra_lines(S, torch, np, dev):
         for i in range(10):
             reps[i % 2][2]()
         step_us = _events_us(torch, lambda i: reps[i % 2][2](), 100)
+        # the same step replayed from one HIP graph per replica
+        graphs = [st.capture_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                                  inp["w_k"], inp["seq_lens"], scale, 1, False)
+                  for inp, st, _ in reps]
+        for i in range(10):
+            graphs[i % 2].replay()
+        graph_us = _events_us(torch, lambda i: graphs[i % 2].replay(), 100)
+        del graphs
 
         def dec(i):
             inp, st, _ = reps[i % 2]
@@ -613,7 +621,8 @@ def extra_lines(S, torch, np, dev):
             "kind": "config", "workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
             "head_dim": d, "block_size": bs, "mode": w.mode,
             "seq_len": int(lens[0]) if w.seq_len else [int(lens.min()), int(lens.max())],
-            "step_us": round(step_us, 2), "decode_us": round(dec_us, 2),
+            "step_us": round(step_us, 2), "step_us_graph_replay": round(graph_us, 2),
+            "decode_us": round(dec_us, 2),
             "decode_GBps": round(dec_alg / (dec_us * 1e-6) / 1e9, 1),
             "decode_frac_of_peak": round(dec_alg / (dec_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
             "step_GBps": round(step_alg / (step_us * 1e-6) / 1e9, 1),
