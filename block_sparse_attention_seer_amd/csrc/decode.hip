@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
         const int row = min(tok0[nt] + ln, last) - blk * BS;  // within the block
         const uint16_t* kp = kc + row * p.st + 8 * lq;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kr[nt][s] = ld16(kp + 32 * s);
+        for (int s = 0; s < KS; ++s) kr[nt][s] = ld16_stream(kp + 32 * s);
       } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) kr[nt][s] = make_uint4(0u, 0u, 0u, 0u);
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
           const int row = min(tok0[nt] + 4 * lq + r, last) - blk * BS;
           const uint16_t* vp = vc + row * p.st + 4 * ln;
 #pragma unroll
-          for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = ld8(vp + 64 * hh);
+          for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = ld8_stream(vp + 64 * hh);
         } else {
 #pragma unroll
           for (int hh = 0; hh < VH; ++hh) vr[nt][r][hh] = make_uint2(0u, 0u);

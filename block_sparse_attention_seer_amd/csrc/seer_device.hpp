@@ -46,6 +46,20 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// The same loads marked non-temporal, for data read once per call (the
+// decode's K and V rows): the caches keep what is reused instead (measured
+// on MI355X: the sparse decode 44.6 -> 41.3 us on 218 MB).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8_stream(const uint16_t* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // Part m (0, 1, 2) of the exact three-way bf16 split x = q0 + q1 + q2 (+ a
 // remainder below 2^-24 |x|): q0 = bf16(x), q1 = bf16(x - q0), q2 =
 // bf16(x - q0 - q1).  Each subtraction is exact in float32 (the operands
