@@ -9,12 +9,12 @@ default workload is the Qwen3-14B-shaped batch (16 sequences, 40 query / 8 KV he
 blocks, top-k 52 of 512 blocks = 90% sparsity).  Inputs are synthetic and
 already resident in HBM.  To keep the 256 MB Infinity Cache from serving
 repeated reads, the timed loop cycles through 24 independent replicas of
-the inputs (each step touches a different one).  The K and V rows are read
-with non-temporal loads and pass the Infinity Cache by; the other per-step
-data (compressed cache, W_q, q, split partials: about 21 MB per replica)
-does stay there, so the replicas together must hold well over 256 MB of it
-(24 x 21 MB; with 16 replicas a step still measures 0.5 us faster, with 24
-and 32 the same).
+the inputs (each step touches a different one).  The V rows are read with
+non-temporal loads and pass the Infinity Cache by; the rest (the selected K
+rows, compressed cache, W_q, q, split partials: about 130 MB per replica)
+does stay there, so the replicas together must hold well over 256 MB of it.
+Even the 21 MB that is not K needs more than 16 replicas: with only that
+kept, 16 replicas measured 0.5 us per step faster, 24 and 32 the same.
 
 Prints one JSON line: µs per step (lower is better), achieved HBM bandwidth
 of the decode kernel on its algorithmic bytes against the 8 TB/s peak, the

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
         const int row = min(tok0[nt] + ln, last) - blk * BS;  // within the block
         const uint16_t* kp = kc + row * p.st + 8 * lq;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kr[nt][s] = ld16_stream(kp + 32 * s);
+        for (int s = 0; s < KS; ++s) kr[nt][s] = ld16(kp + 32 * s);
       } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) kr[nt][s] = make_uint4(0u, 0u, 0u, 0u);

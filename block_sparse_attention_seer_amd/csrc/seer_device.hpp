@@ -46,15 +46,14 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// The same loads marked non-temporal, for data read once per call (the
-// decode's K and V rows): the caches keep what is reused instead (measured
-// on MI355X: the sparse decode 44.6 -> 41.3 us on 218 MB).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// An 8-byte load marked non-temporal (`global_load ... nt`), for data read
+// once per call that nothing waits on first: the decode's V rows.  Such loads
+// do not allocate in the Infinity Cache, which keeps it and its allocation
+// bandwidth for other traffic.  On MI355X they cost latency, so the K rows,
+// which every chunk's scores wait on, use ordinary loads: streaming V only
+// was measured faster than streaming both at every size from batch 1 at 8k
+// tokens (latency-bound) to batch 64 at 64k (bandwidth-bound).
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 __device__ __forceinline__ uint2 ld8_stream(const uint16_t* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
