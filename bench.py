@@ -677,6 +677,111 @@ def extra_lines(S, torch, np, dev):
     del inp, st, runs
     torch.cuda.empty_cache()
 
+    # ---- the benchmarked workload over a paged KV cache, and with top-p
+    w = WORKLOADS["qwen3_14b_b16"]
+    log("extra: paged cache and top-p on qwen3_14b_b16")
+    B, Hq, Hkv, d, dg, bs = (w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                             w.block_size)
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
+    scale = 1.0 / math.sqrt(d)
+    inp = make_inputs(w, device=str(dev))
+    lens = inp["seq_lens"].cpu().numpy()
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=dev)
+    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    run_topk = st.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                            inp["w_k"], inp["seq_lens"], scale, 1, False)
+    run_topk()
+    # one page per gate block of every KV head, scattered over the pool in a
+    # seeded random order
+    nbm = w.max_seq_len // bs
+    perm = torch.randperm(B * nbm, generator=torch.Generator().manual_seed(w.seed + 17))
+    perm_d = perm.to(dev)
+
+    def to_pool(x):
+        pool = torch.empty((B * nbm, Hkv, bs, d), dtype=x.dtype, device=dev)
+        pool[perm_d] = x.view(B, Hkv, nbm, bs, d).transpose(1, 2).reshape(B * nbm, Hkv, bs, d)
+        return pool
+
+    kp, vp = to_pool(inp["k"]), to_pool(inp["v"])
+    table = perm.view(B, nbm).to(torch.int32).to(dev)
+    dn = _dense_buffers(S, torch, dims, dev)
+
+    def dec(i):
+        S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], st.block_idx,
+                             st.num_selected, st.max_selected, scale, st.num_split,
+                             st.decode_ws, st.out, st.lse)
+
+    def dec_paged(i):
+        S.seer_sparse_decode_paged(dims, inp["q"], kp, vp, table, inp["seq_lens"], st.block_idx,
+                                   st.num_selected, st.max_selected, scale, st.num_split,
+                                   st.decode_ws, st.out, st.lse)
+
+    def dense(i):
+        S.seer_dense_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], scale, *dn)
+
+    def dense_paged(i):
+        S.seer_dense_decode_paged(dims, inp["q"], kp, vp, table, inp["seq_lens"], scale, *dn)
+
+    dec(0)
+    ref = st.out.clone()
+    dec_paged(0)
+    same = bool(torch.equal(ref, st.out))
+    dense(0)
+    ref = dn[2].clone()
+    dense_paged(0)
+    same_dense = bool(torch.equal(ref, dn[2]))
+    t = {f.__name__: _flushed_median_us(torch, f, 30 if f.__name__.startswith("dec") else 10,
+                                        flush)
+         for f in (dec, dec_paged, dense, dense_paged)}
+    sel = _selected_tokens(st, lens, bs)
+    blocks = int(st.num_selected.sum().item())
+    qo = 2 * B * Hq * d * 2
+    alg = sel * 2 * d * 2 + qo + B * Hkv * (st.max_selected + 1) * 4
+    print(json.dumps({
+        "kind": "paged", "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+        "head_dim": d, "block_size": bs, "seq_len": int(lens[0]), "pages": B * nbm,
+        "sparse_decode_us": round(t["dec"], 2), "sparse_decode_paged_us": round(t["dec_paged"], 2),
+        "sparse_paged_GBps": round((alg + 4 * blocks) / (t["dec_paged"] * 1e-6) / 1e9, 1),
+        "sparse_paged_frac_of_peak": round((alg + 4 * blocks) / (t["dec_paged"] * 1e-6) / 1e9
+                                           / PEAK_GBPS, 4),
+        "dense_decode_us": round(t["dense"], 2), "dense_decode_paged_us": round(t["dense_paged"], 2),
+        "paged_equals_contiguous": same and same_dense,
+        "timing": "median of per-launch event pairs, 1 GiB read before each",
+    }), flush=True)
+    del kp, vp, table, perm_d
+
+    # top-p over the same inputs: the whole step, then its decode alone
+    for p_mass in (0.9, 0.99):
+        stp = S.DecodeStep(dims, mode=S.SELECT_TOPP, threshold=p_mass, device=dev)
+        stp.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+        run = stp.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                            inp["w_k"], inp["seq_lens"], scale, 1, False)
+        run()
+
+        def dec_p(i):
+            S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"],
+                                 stp.block_idx, stp.num_selected, stp.max_selected, scale,
+                                 stp.num_split, stp.decode_ws, stp.out, stp.lse)
+
+        step_us = _flushed_median_us(torch, lambda i: run(), 30, flush)
+        dec_us = _flushed_median_us(torch, dec_p, 30, flush)
+        sel_p = _selected_tokens(stp, lens, bs)
+        alg_p = sel_p * 2 * d * 2 + qo + B * Hkv * (stp.max_selected + 1) * 4
+        print(json.dumps({
+            "kind": "topp", "workload": w.name, "p": p_mass, "batch": B, "q_heads": Hq,
+            "kv_heads": Hkv, "seq_len": int(lens[0]),
+            "step_us": round(step_us, 2), "decode_us": round(dec_us, 2),
+            "decode_GBps": round(alg_p / (dec_us * 1e-6) / 1e9, 1),
+            "decode_frac_of_peak": round(alg_p / (dec_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+            "selected_fraction": round(sel_p / float(lens.sum() * Hkv), 4),
+            "dense_decode_us": round(t["dense"], 2),
+            "speedup_vs_dense_step": round(t["dense"] / step_us, 3),
+            "timing": "median of per-launch event pairs, 1 GiB read before each",
+        }), flush=True)
+        del stp
+    del inp, st, run_topk, dn
+    torch.cuda.empty_cache()
+
     # ---- the pages' microbenchmark grid: kernel-level sparse vs dense
     base = WORKLOADS["qwen3_8b_layer"]
     for B in (1, 4, 16):
