@@ -94,8 +94,9 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--extra", action="store_true",
                     help="instead of the headline line: one JSON line each for the Qwen3-8B-shaped "
-                         "layer, the 64-sequence threshold batch, the 256-step 128k pipeline and "
-                         "the pages' microbenchmark grid (64/8 heads, batch 1/4/16, 8k/32k/128k, "
+                         "layer, the 64-sequence threshold batch, the 256-step 128k pipeline, "
+                         "the benchmarked batch over a paged cache and with top-p, and the pages' "
+                         "microbenchmark grid (64/8 heads, batch 1/4/16, 8k/32k/128k, "
                          "50%%/90%% sparsity)")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a few decode launches and a plain copy of "
@@ -750,7 +751,9 @@ def extra_lines(S, torch, np, dev):
     }), flush=True)
     del kp, vp, table, perm_d
 
-    # top-p over the same inputs: the whole step, then its decode alone
+    # top-p over the same inputs: the fused step (whose decode divides the
+    # uneven selections evenly over the grid when there are fewer pairs than
+    # compute units), then the standalone decode call with fixed splits
     for p_mass in (0.9, 0.99):
         stp = S.DecodeStep(dims, mode=S.SELECT_TOPP, threshold=p_mass, device=dev)
         stp.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
@@ -770,9 +773,10 @@ def extra_lines(S, torch, np, dev):
         print(json.dumps({
             "kind": "topp", "workload": w.name, "p": p_mass, "batch": B, "q_heads": Hq,
             "kv_heads": Hkv, "seq_len": int(lens[0]),
-            "step_us": round(step_us, 2), "decode_us": round(dec_us, 2),
-            "decode_GBps": round(alg_p / (dec_us * 1e-6) / 1e9, 1),
-            "decode_frac_of_peak": round(alg_p / (dec_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+            "step_us": round(step_us, 2), "decode_fixed_splits_us": round(dec_us, 2),
+            "decode_fixed_splits_GBps": round(alg_p / (dec_us * 1e-6) / 1e9, 1),
+            "decode_fixed_splits_frac_of_peak": round(alg_p / (dec_us * 1e-6) / 1e9 / PEAK_GBPS,
+                                                      4),
             "selected_fraction": round(sel_p / float(lens.sum() * Hkv), 4),
             "dense_decode_us": round(t["dense"], 2),
             "speedup_vs_dense_step": round(t["dense"] / step_us, 3),

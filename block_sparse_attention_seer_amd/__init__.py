@@ -460,12 +460,16 @@ class DecodeStep:
         self.num_selected = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         gws = seer_gate_workspace_bytes(dims)
         self.gate_ws = torch.zeros((max(gws, 16) // 4 + 4,), dtype=torch.float32, device=dev)
+        # the caller's request (0 = automatic) goes to the fused step, which
+        # may then divide uneven selections evenly over the grid (stream-K);
+        # the staged decode calls use the resolved split count
+        self.split_request = int(num_split)
         self.num_split = seer_decode_num_split(dims, self.max_selected, num_split)
         dws = seer_decode_workspace_bytes(dims, self.max_selected, self.num_split)
         self.decode_ws = torch.zeros((max(dws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, Hq, dims.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        sws = seer_decode_step_workspace_bytes(dims, self.max_selected, self.num_split)
+        sws = seer_decode_step_workspace_bytes(dims, self.max_selected, self.split_request)
         self.step_ws = torch.zeros((max(sws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
 
     @property
@@ -536,7 +540,7 @@ class DecodeStep:
                                  self.kcomp_lens, self.kcomp, max_new_blocks, self.rope_theta,
                                  self.mode, self.topk_blocks, self.threshold, self.max_selected,
                                  self.block_idx, self.num_selected,
-                                 self.logits if keep_logits else None, scale, self.num_split,
+                                 self.logits if keep_logits else None, scale, self.split_request,
                                  self.step_ws, self.out, self.lse)
         fn = lib().seer_decode_step
         dev = q.device
@@ -559,5 +563,5 @@ class DecodeStep:
                          self.kcomp_lens, self.kcomp, max_new_blocks, self.rope_theta, self.mode,
                          self.topk_blocks, self.threshold, self.max_selected, self.block_idx,
                          self.num_selected, self.logits if keep_logits else None, scale,
-                         self.num_split, self.step_ws, self.out, self.lse)
+                         self.split_request, self.step_ws, self.out, self.lse)
         return self.out, self.lse

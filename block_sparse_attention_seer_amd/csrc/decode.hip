@@ -88,19 +88,30 @@ __device__ __forceinline__ uint32_t pick2(uint2 a, uint2 b, int j) {
   return (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
 }
 
-template <int D, int BS, bool DENSE, int NW, bool PAGED>
-__global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
+// The part of one (b, h) that a workgroup computes.  Fixed splits cut the
+// pair's active chunks into num_split even ranges and take range `split`;
+// stream-K parts carry their chunk range [c_begin, c_end).  A pair of more
+// than one part leaves each part's result in a slot of the workspace: part 0
+// in slot0, part k > 0 in slot1 + (k - 1) * slot_step.
+struct Part {
+  int pair;
+  int split, num_split;  // fixed splits
+  int c_begin, c_end;    // stream-K
+  int nparts;
+  int64_t my_slot, slot0, slot1, slot_step;
+};
+
+template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK>
+__device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& pt, float* sm_o) {
   constexpr int TPC = kTilesPerChunk;  // 16-token tiles per chunk
   constexpr int KS = D / 32;   // k-steps of the score contraction
   constexpr int VH = D / 64;   // 64-dim halves of the value contraction
+  constexpr int CPB = BS / (16 * TPC);  // chunks per block
 
-  extern __shared__ float sm_o[];  // [NW][G][D]
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
 
-  const int S = p.num_split;
-  const int pair = blockIdx.x / S;
-  const int split = blockIdx.x - pair * S;
+  const int pair = pt.pair;
   const int b = pair / p.Hkv;
   const int h = pair - b * p.Hkv;
   const int tid = threadIdx.x;
@@ -110,20 +121,17 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   const int lq = lane >> 4;
   const int G = p.G;
 
-  // Fused step: the cache entries appended by this step's gate launch are
-  // counted now, after every reader of the old count has finished.
-  if (p.commit_lens != nullptr && blockIdx.x == 0) {
-    for (int bb = tid; bb < p.B; bb += NW * 64)
-      p.commit_lens[bb] = committed_count(p.seq_lens[bb], p.commit_lens[bb], p.BS, p.Lmax, p.NBmax,
-                                          p.commit_max_new);
-  }
-
   const int32_t* idx = DENSE ? nullptr : p.block_idx + static_cast<int64_t>(pair) * p.max_sel;
   // The first kIdxLds entries of the index row go to LDS, requested at once
   // with the selection count instead of after it.
   __shared__ int s_idx[kIdxLds];
-  if (!DENSE)
-    for (int i = tid; i < min(p.max_sel, kIdxLds); i += NW * 64) s_idx[i] = idx[i];
+  if (!DENSE) {
+    // a stream-K part stages only the entries of its own chunks
+    const int i_end = min(p.max_sel, kIdxLds);
+    const int i_lo = SK ? min(pt.c_begin / CPB, i_end) : 0;
+    const int i_hi = SK ? min((pt.c_end + CPB - 1) / CPB, i_end) : i_end;
+    for (int i = i_lo + tid; i < i_hi; i += NW * 64) s_idx[i] = idx[i];
+  }
   // paged cache: this sequence's block-table row, requested with the rest
   __shared__ int s_table[PAGED ? kTableLds : 1];
   if (PAGED)
@@ -145,10 +153,12 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   // split takes chunks c_begin + w, c_begin + w + NW, ...  (A fixed
   // assignment keeps the summation order, and so the output bits, the same
   // from run to run.)
-  constexpr int CPB = BS / (16 * TPC);  // chunks per block
   const int nchunks = nslots * CPB;
-  const int c_begin = static_cast<int>(static_cast<int64_t>(nchunks) * split / S);
-  const int c_end = static_cast<int>(static_cast<int64_t>(nchunks) * (split + 1) / S);
+  const int c_begin =
+      SK ? pt.c_begin : static_cast<int>(static_cast<int64_t>(nchunks) * pt.split / pt.num_split);
+  const int c_end = SK ? min(pt.c_end, nchunks)
+                       : static_cast<int>(static_cast<int64_t>(nchunks) * (pt.split + 1) /
+                                          pt.num_split);
 
   const uint16_t* kb = p.k + b * p.sb + h * p.sh;
   const uint16_t* vb = p.v + b * p.sb + h * p.sh;
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 
   const int nel = G * D;
   const int64_t out_base = static_cast<int64_t>(b) * p.Hq + h * G;
-  const int64_t part = static_cast<int64_t>(pair) * S + split;
+  const int64_t part = pt.my_slot;
   for (int e = tid; e < nel; e += NW * 64) {
     const int head = e / D;
     const int dim = e - head * D;
@@ -338,7 +348,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     }
     const bool any = lsum > 0.f;
     const float o = any ? osum / lsum : 0.f;
-    if (S == 1) {
+    if (pt.nparts == 1) {
       p.out[(out_base + head) * D + dim] = f2bf(o);
       if (dim == 0 && p.lse != nullptr)
         p.lse[out_base + head] = any ? (M + fast_log2(lsum)) * kLn2 : -INFINITY;
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (S == 1 || p.counters == nullptr) return;
+  if (pt.nparts == 1 || p.counters == nullptr) return;
 
   // ---- the last split of this (b, h) to finish merges all splits.
   // Partials travel only through device-coherent stores and loads, so the
@@ -370,12 +380,12 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   if (tid == 0) {
     const int prev = __hip_atomic_fetch_add(p.counters + pair, 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = (prev == S - 1);
+    sm_last = (prev == pt.nparts - 1);
   }
   __syncthreads();
   if (!sm_last) return;
-  const float* plse = p.part_lse + static_cast<int64_t>(pair) * S * G;
-  const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
+  const int S = pt.nparts;
+  auto slot_of = [&](int k) -> int64_t { return k == 0 ? pt.slot0 : pt.slot1 + (k - 1) * pt.slot_step; };
   if (S <= kMergeInline) {
     // one round trip: each element's S partial outputs and its head's S
     // partial lse values are requested together; the weights are formed per
@@ -387,8 +397,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int s = 0; s < kMergeInline; ++s) {
         if (s < S) {
-          ls[s] = __hip_atomic_load(plse + s * G + head, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          os[s] = __hip_atomic_load(po + (s * G + head) * D + dim, __ATOMIC_RELAXED,
+          const int64_t sl = slot_of(s);
+          ls[s] = __hip_atomic_load(p.part_lse + sl * G + head, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+          os[s] = __hip_atomic_load(p.part_o + (sl * G + head) * D + dim, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -412,9 +424,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
       if (dim == 0 && p.lse != nullptr)
         p.lse[out_base + head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
     }
-  } else {
+  } else if (S <= kMaxSplit) {
     for (int i = tid; i < S * G; i += NW * 64)
-      sm_w[i] = __hip_atomic_load(plse + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm_w[i] = __hip_atomic_load(p.part_lse + slot_of(i / G) * G + i % G, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (tid < G) {
       const int head = tid;
@@ -437,13 +450,199 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
       const int dim = e - head * D;
       float o = 0.f;
       for (int s = 0; s < S; ++s)
-        o += sm_w[s * G + head] * __hip_atomic_load(po + (s * G + head) * D + dim, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+        o += sm_w[s * G + head] * __hip_atomic_load(p.part_o + (slot_of(s) * G + head) * D + dim,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       p.out[(out_base + head) * D + dim] = f2bf(o);
+      if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
+    }
+  } else {
+    // More parts than the weights held in LDS (a stream-K pair cut over
+    // many workgroups): the same weights, in the same order, formed and
+    // applied kMaxSplit parts at a time.
+    __shared__ float sm_mx[16];
+    __shared__ float sm_inv[16];
+    if (tid < G) {
+      const int head = tid;
+      float M = -INFINITY;
+      for (int s = 0; s < S; ++s)
+        M = fmaxf(M, __hip_atomic_load(p.part_lse + slot_of(s) * G + head, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT));
+      float tot = 0.f;
+      for (int s = 0; s < S; ++s) {
+        const float ls = __hip_atomic_load(p.part_lse + slot_of(s) * G + head, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        tot += (M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
+      }
+      sm_mx[head] = M;
+      sm_inv[head] = tot > 0.f ? 1.f / tot : 0.f;
+      sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
+    }
+    constexpr int EPT = (kMaxGroup * D + NW * 64 - 1) / (NW * 64);
+    float acc[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) acc[i] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kMaxSplit) {
+      const int ns = min(kMaxSplit, S - s0);
+      __syncthreads();  // sm_mx, sm_inv ready; the previous batch's weights consumed
+      for (int i = tid; i < ns * G; i += NW * 64) {
+        const int head = i % G;
+        const float ls = __hip_atomic_load(p.part_lse + slot_of(s0 + i / G) * G + head,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float M = sm_mx[head];
+        sm_w[i] = ((M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M)) * sm_inv[head];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const int e = tid + i * NW * 64;
+        if (e >= nel) break;
+        const int head = e / D;
+        const int dim = e - head * D;
+        for (int s = 0; s < ns; ++s)
+          acc[i] += sm_w[s * G + head] *
+                    __hip_atomic_load(p.part_o + (slot_of(s0 + s) * G + head) * D + dim,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + i * NW * 64;
+      if (e >= nel) break;
+      const int head = e / D;
+      const int dim = e - head * D;
+      p.out[(out_base + head) * D + dim] = f2bf(acc[i]);
       if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
     }
   }
   if (tid == 0) __hip_atomic_store(p.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Index of the stream-K workgroup whose chunk range holds global chunk x:
+// workgroup w takes [floor(w T / N), floor((w + 1) T / N)).
+__device__ __forceinline__ int sk_group_of(int x, int T, int N) {
+  return min(static_cast<int>((static_cast<int64_t>(x + 1) * N - 1) / T), N - 1);
+}
+
+// Fixed splits: workgroup = (pair, split).  Stream-K (uneven selections):
+// every workgroup takes an equal share of all pairs' active chunks, found
+// from a prefix over num_selected, and decodes the pairs that share overlaps
+// one after another.  A pair inside one share writes its output directly; a
+// pair cut between shares is merged by the last of its parts to finish, as
+// fixed splits are.  Nothing waits on another workgroup in either scheme.
+template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK>
+__global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
+  extern __shared__ float sm_o[];  // [NW][G][D]
+  const int tid = threadIdx.x;
+
+  // Fused step: the cache entries appended by this step's gate launch are
+  // counted now, after every reader of the old count has finished.
+  if (p.commit_lens != nullptr && blockIdx.x == 0) {
+    for (int bb = tid; bb < p.B; bb += NW * 64)
+      p.commit_lens[bb] = committed_count(p.seq_lens[bb], p.commit_lens[bb], p.BS, p.Lmax, p.NBmax,
+                                          p.commit_max_new);
+  }
+
+  if constexpr (!SK) {
+    Part pt{};
+    pt.num_split = p.num_split;
+    pt.pair = blockIdx.x / pt.num_split;
+    pt.split = blockIdx.x - pt.pair * pt.num_split;
+    pt.nparts = pt.num_split;
+    pt.slot0 = static_cast<int64_t>(pt.pair) * pt.num_split;
+    pt.my_slot = pt.slot0 + pt.split;
+    pt.slot1 = pt.slot0 + 1;
+    pt.slot_step = 1;
+    decode_part<D, BS, DENSE, NW, PAGED, false>(p, pt, sm_o);
+  } else {
+    static_assert(!DENSE, "stream-K division is for selections");
+    constexpr int CPB = BS / (16 * kTilesPerChunk);
+    constexpr int NT = NW * 64;
+    __shared__ int s_pre[kSkMaxPairs + 1];  // prefix of the pairs' chunk counts
+    __shared__ int s_run[NT];
+    const int P = p.B * p.Hkv;  // at most kSkMaxPairs (checked on the host)
+    const int per = (P + NT - 1) / NT;
+    const int i0 = min(tid * per, P);
+    const int i1 = min(i0 + per, P);
+    int run = 0;
+    for (int i = i0; i < i1; ++i) {
+      const int n = min(max(p.num_selected[i], 0), p.max_sel) * CPB;
+      s_pre[i + 1] = n;
+      run += n;
+    }
+    s_run[tid] = run;
+    __syncthreads();
+    if (tid < 64) {  // wave 0: exclusive scan of the NT per-thread totals
+      int v[NW];
+      int t = 0;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        v[j] = s_run[tid * NW + j];
+        t += v[j];
+      }
+      int incl = t;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (tid >= o) incl += y;
+      }
+      int ex = incl - t;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        s_run[tid * NW + j] = ex;
+        ex += v[j];
+      }
+    }
+    __syncthreads();
+    {
+      int acc = s_run[tid];
+      if (tid == 0) s_pre[0] = 0;
+      for (int i = i0; i < i1; ++i) {
+        acc += s_pre[i + 1];
+        s_pre[i + 1] = acc;
+      }
+    }
+    __syncthreads();
+    const int T = s_pre[P];
+    const int grid = static_cast<int>(gridDim.x);
+    const int wg = static_cast<int>(blockIdx.x);
+    const int G = p.G;
+    // pairs without an active chunk: output 0, lse -inf
+    for (int q = wg; q < P; q += grid) {
+      if (s_pre[q + 1] != s_pre[q]) continue;
+      const int bq = q / p.Hkv;
+      const int64_t ob = static_cast<int64_t>(bq) * p.Hq + (q - bq * p.Hkv) * G;
+      for (int e = tid; e < G * D; e += NT) p.out[ob * D + e] = 0;
+      if (tid < G && p.lse != nullptr) p.lse[ob + tid] = -INFINITY;
+    }
+    const int N = min(grid, T);  // every one of these shares is non-empty
+    if (wg >= N) return;
+    const int lo = static_cast<int>(static_cast<int64_t>(wg) * T / N);
+    const int hi = static_cast<int>(static_cast<int64_t>(wg + 1) * T / N);
+    int q = 0;  // first pair ending past lo
+    for (int z = P - 1; q < z;) {
+      const int m = (q + z) >> 1;
+      if (s_pre[m + 1] > lo) z = m; else q = m + 1;
+    }
+    for (; q < P && s_pre[q] < hi; ++q) {
+      const int base = s_pre[q];
+      const int cnt = s_pre[q + 1] - base;
+      if (cnt == 0) continue;
+      const int w0 = sk_group_of(base, T, N);
+      Part pt{};
+      pt.pair = q;
+      pt.c_begin = max(lo, base) - base;
+      pt.c_end = min(hi, base + cnt) - base;
+      pt.nparts = sk_group_of(base + cnt - 1, T, N) - w0 + 1;
+      // slot 2w holds the part of the pair a share starts in, 2w + 1 the
+      // part of the pair that starts inside the share and runs past it
+      pt.slot0 = 2 * static_cast<int64_t>(w0) +
+                 (base == static_cast<int>(static_cast<int64_t>(w0) * T / N) ? 0 : 1);
+      pt.slot1 = 2 * static_cast<int64_t>(w0 + 1);
+      pt.slot_step = 2;
+      pt.my_slot = (wg == w0) ? pt.slot0 : 2 * static_cast<int64_t>(wg);
+      decode_part<D, BS, false, NW, PAGED, true>(p, pt, sm_o);
+    }
+  }
 }
 
 // Merge of the splits of one (b, h): o = sum_s w_s o_s with
@@ -514,11 +713,22 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
   }
 }
 
-template <int D, int BS, bool DENSE, int NW, bool PAGED>
+template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK = false>
 void launch_one(const DecodeParams& p, int grid, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(NW) * p.G * D * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW, PAGED>), dim3(grid), dim3(NW * 64), lds,
+  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW, PAGED, SK>), dim3(grid), dim3(NW * 64), lds,
                      stream, p);
+}
+
+// stream-K: selections over a contiguous cache
+template <int NW>
+void launch_variant_sk(int key, const DecodeParams& p, int grid, hipStream_t s) {
+  switch (key) {
+    case 0: launch_one<64, 64, false, NW, false, true>(p, grid, s); break;
+    case 2: launch_one<64, 128, false, NW, false, true>(p, grid, s); break;
+    case 4: launch_one<128, 64, false, NW, false, true>(p, grid, s); break;
+    default: launch_one<128, 128, false, NW, false, true>(p, grid, s); break;
+  }
 }
 
 template <int NW, bool PAGED>
@@ -571,11 +781,22 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   p.page_stride = a.page_stride;
   p.page_head_stride = a.page_head_stride;
   const bool inline_merge = a.merge_inline;
-  if (S > 1) {
+  const bool dense = (a.block_idx == nullptr);
+  const bool paged = a.block_table != nullptr;
+  const int wpg = a.waves_per_group;
+  const int nw = ((wpg == 4 || wpg == 8) && decode_waves_fit(wpg, G, d.head_dim))
+                     ? wpg
+                     : decode_waves_per_group(G, d.head_dim);
+  // stream-K where it applies: a selection over a contiguous cache, merged in
+  // the launch, with the pairs' prefix and the wave merge both in LDS
+  const bool sk = a.stream_k && !dense && !paged && inline_merge && pairs <= kSkMaxPairs &&
+                  static_cast<int64_t>(nw) * G * d.head_dim * 4 <= kSkMergeLds;
+  if (S > 1 || sk) {
     char* ws = static_cast<char*>(a.workspace);
     size_t cbytes = static_cast<size_t>(pairs) * sizeof(int32_t);
     cbytes = (cbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
-    size_t lbytes = static_cast<size_t>(pairs) * S * G * sizeof(float);
+    // stream-K: two partial slots per workgroup
+    size_t lbytes = static_cast<size_t>(pairs) * S * (sk ? 2 : 1) * G * sizeof(float);
     lbytes = (lbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
     p.counters = inline_merge ? reinterpret_cast<int32_t*>(ws) : nullptr;
     p.part_lse = reinterpret_cast<float*>(ws + cbytes);
@@ -588,14 +809,10 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   }
   const int grid = static_cast<int>(grid64);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool dense = (a.block_idx == nullptr);
   const int key = (d.head_dim == 128 ? 4 : 0) | (d.block_size == 128 ? 2 : 0) | (dense ? 1 : 0);
-  const int wpg = a.waves_per_group;
-  const int nw = ((wpg == 4 || wpg == 8) && decode_waves_fit(wpg, G, d.head_dim))
-                     ? wpg
-                     : decode_waves_per_group(G, d.head_dim);
-  const bool paged = a.block_table != nullptr;
-  if (nw == 8)
+  if (sk)
+    nw == 8 ? launch_variant_sk<8>(key, p, grid, s) : launch_variant_sk<4>(key, p, grid, s);
+  else if (nw == 8)
     paged ? launch_variant<8, true>(key, p, grid, s) : launch_variant<8, false>(key, p, grid, s);
   else
     paged ? launch_variant<4, true>(key, p, grid, s) : launch_variant<4, false>(key, p, grid, s);
@@ -604,7 +821,7 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
     set_error(std::string("decode launch: ") + hipGetErrorString(e));
     return SEER_ERR_HIP;
   }
-  if (S > 1 && !inline_merge) {
+  if (S > 1 && !inline_merge && !sk) {
     if (d.head_dim == 128)
       hipLaunchKernelGGL(combine_kernel<128>, dim3(grid64 / S), dim3(kCombineThreads), 0, s, p);
     else

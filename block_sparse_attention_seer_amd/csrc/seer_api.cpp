@@ -225,7 +225,7 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
                          int32_t num_split, void* workspace, size_t workspace_bytes,
                          uint16_t* out, float* lse, void* stream,
                          int32_t* commit_lens = nullptr, int commit_max_new = 0,
-                         const PagedCache* paged = nullptr) {
+                         const PagedCache* paged = nullptr, bool stream_k = false) {
   SEER_CHECK(check_dims(dims, &why_));
   SEER_CHECK(check_ptr(q, 16, "q", &why_));
   SEER_CHECK(check_ptr(k, 16, "k_cache", &why_));
@@ -240,9 +240,14 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
   int rc = resolve_split(dims, max_blocks, num_split, &s);
   if (rc != SEER_OK) return rc;
   const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
-  const size_t need = seer::decode_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
-                                                   dims->head_dim);
-  if (need > 0) {
+  const int g = dims->num_q_heads / dims->num_kv_heads;
+  const size_t need = seer::decode_workspace_bytes(pairs, s, g, dims->head_dim);
+  // stream-K only with the workspace it needs (the fused step provides it)
+  stream_k = stream_k && workspace != nullptr &&
+             workspace_bytes >= seer::decode_sk_workspace_bytes(pairs, s, g, dims->head_dim);
+  if (stream_k) {
+    SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
+  } else if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(SEER_ERR_WORKSPACE, "decode workspace missing or smaller than seer_decode_workspace_bytes()");
     SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
@@ -250,6 +255,7 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
   seer::DecodeArgs a{q, k, v, seq_lens, block_idx, num_selected, max_blocks, scale, s,
                      tuning_waves(), tuning_merge_inline(), workspace, out, lse,
                      commit_lens, commit_max_new};
+  a.stream_k = stream_k;
   if (paged != nullptr) {
     SEER_CHECK(check_paged(dims, *paged, &why_));
     a.block_table = paged->block_table;
@@ -351,10 +357,27 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
     if (rc != SEER_OK) return rc;
   }
   const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
-  const size_t dec_bytes = seer::decode_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
-                                                        dims->head_dim);
+  const int g = dims->num_q_heads / dims->num_kv_heads;
+  size_t dec_bytes = seer::decode_workspace_bytes(pairs, s, g, dims->head_dim);
   if (workspace == nullptr || workspace_bytes < dec_bytes + seer::step_gate_bytes(dims))
     return fail(SEER_ERR_WORKSPACE, "workspace missing or smaller than seer_decode_step_workspace_bytes()");
+  // Threshold and top-p keep a different number of blocks per pair.  With
+  // fewer pairs than compute units, fixed splits cannot even that out, so
+  // with an automatic split count their decode divides all chunks evenly
+  // over the grid (stream-K) when the workspace holds its larger decode
+  // region.  With more pairs the dispatcher balances the fixed splits
+  // itself, and stream-K's extra part boundaries measured slower.
+  bool stream_k = false;
+  int cus = 0;
+  if (num_split == 0 && mode != SEER_SELECT_TOPK && seer::device_cu_count(&cus) == SEER_OK &&
+      pairs < cus) {
+    const size_t sk_bytes =
+        std::max(dec_bytes, seer::decode_sk_workspace_bytes(pairs, s, g, dims->head_dim));
+    if (workspace_bytes >= sk_bytes + seer::step_gate_bytes(dims)) {
+      dec_bytes = sk_bytes;
+      stream_k = true;
+    }
+  }
   SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
   if (max_new_blocks > seer::nb_max(dims)) max_new_blocks = static_cast<int32_t>(seer::nb_max(dims));
 
@@ -402,7 +425,7 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   if (rc != SEER_OK) return rc;
   return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,
                        scale, s, workspace, dec_bytes, out, lse, stream,
-                       inline_new > 0 ? kcomp_lens : nullptr, inline_new);
+                       inline_new > 0 ? kcomp_lens : nullptr, inline_new, nullptr, stream_k);
 }
 
 size_t seer_prefill_workspace_bytes(const seer_dims* dims) {
@@ -436,7 +459,15 @@ size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selec
                                         int32_t num_split) {
   std::string why;
   if (check_dims(dims, &why) != SEER_OK || max_selected < 1) return 0;
-  return seer_decode_workspace_bytes(dims, max_selected, num_split) + seer::step_gate_bytes(dims);
+  size_t dec = seer_decode_workspace_bytes(dims, max_selected, num_split);
+  if (num_split == 0) {  // room for the stream-K decode of threshold and top-p
+    int s = 0;
+    if (resolve_split(dims, max_selected, 0, &s) != SEER_OK) return 0;
+    const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
+    dec = std::max(dec, seer::decode_sk_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
+                                                        dims->head_dim));
+  }
+  return dec + seer::step_gate_bytes(dims);
 }
 
 }  // extern "C"

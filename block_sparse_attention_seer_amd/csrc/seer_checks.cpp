@@ -108,6 +108,15 @@ size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim)
   return counters + lse + parts * head_dim * sizeof(float);
 }
 
+size_t decode_sk_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim) {
+  size_t counters = static_cast<size_t>(pairs) * sizeof(int32_t);
+  counters = (counters + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
+  const size_t parts = static_cast<size_t>(pairs) * (num_split > 1 ? num_split : 1) * 2 * g;
+  size_t lse = parts * sizeof(float);
+  lse = (lse + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
+  return counters + lse + parts * head_dim * sizeof(float);
+}
+
 int64_t prefill_padded_len(const seer_dims* d) {
   return (static_cast<int64_t>(d->max_seq_len) + kPrefillTokenTile - 1) / kPrefillTokenTile *
          kPrefillTokenTile;

@@ -18,6 +18,8 @@ constexpr int kDecodeMergeLds = 48 * 1024;  // LDS bytes for the decode wave mer
 constexpr int kMaxInlineNew = 4;       // new cache entries the gate launch computes itself
 constexpr int kCounterBytes = 256;     // alignment of the partial outputs after the partial lse
 constexpr int kPrefillTokenTile = 64;  // prefill: key tile, and the padding of the token axis
+constexpr int kSkMaxPairs = 2048;      // (b, h) pairs the stream-K decode prefixes in LDS
+constexpr int kSkMergeLds = 32 * 1024; // wave-merge LDS bytes that leave room for that prefix
 
 // ------------------------------------------------------- argument checks
 // These live in a HIP-free translation unit so that a CPU-only test can
@@ -34,6 +36,9 @@ size_t step_gate_bytes(const seer_dims* d);
 // Workspace of the decode kernel for `pairs` (b, h) pairs, `num_split`
 // splits and group size g: the per-split lse and outputs.
 size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim);
+// Workspace of the stream-K decode over a grid of pairs x num_split
+// workgroups: a counter per pair and two partial slots per workgroup.
+size_t decode_sk_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim);
 // Automatic split count given the device's compute-unit count.
 int auto_num_split(const seer_dims* d, int max_blocks, int num_cus);
 
@@ -117,6 +122,11 @@ struct DecodeArgs {
   int num_pages;
   int64_t page_stride;
   int64_t page_head_stride;
+  // Divide the selections' chunks evenly over the grid (stream-K) instead of
+  // cutting each pair into num_split ranges.  Needs a workspace of
+  // decode_sk_workspace_bytes(); the launch falls back to fixed splits where
+  // the stream-K kernel does not apply.
+  bool stream_k = false;
 };
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
 

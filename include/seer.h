@@ -308,6 +308,14 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
  * first workgroup also raises kcomp_lens -- so kcomp_lens keeps its old
  * value until then and nothing else may read it in between.
  *
+ * Under SEER_SELECT_THRESHOLD and SEER_SELECT_TOPP the pairs keep different
+ * numbers of blocks.  With num_split = 0, fewer (b, h) pairs than compute
+ * units, and a workspace of at least seer_decode_step_workspace_bytes(dims,
+ * max_selected, 0), launch 2 then divides all pairs' selected chunks evenly
+ * over its grid (stream-K) instead of splitting each pair num_split ways.
+ * The result equals the split decode up to summation order (the same
+ * tolerance to the exact attention), and is the same from run to run.
+ *
  *   q_nope, q        [B, H_q, d] pre-/post-RoPE queries (may alias).
  *   k_nope, k_cache, v_cache  caches (layout above; k_nope may alias k_cache).
  *   w_q, w_k         gate weights.   seq_lens [B] includes the current token.
@@ -321,6 +329,9 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
  *   workspace        >= seer_decode_step_workspace_bytes(dims, max_selected,
  *                    num_split) bytes, 256-byte aligned: the decode workspace
  *                    (zero before first use) followed by the gate queries.
+ *                    With num_split = 0 the size includes the stream-K
+ *                    decode's per-workgroup partials; a workspace sized for
+ *                    the split decode alone is still accepted (no stream-K).
  *   out, lse         as seer_sparse_decode.
  */
 size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selected,

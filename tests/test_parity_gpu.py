@@ -791,7 +791,11 @@ def _clone_state(st_from, st_to):
     ("tiny", dict(seq_len=1000, mode="topp", tau=0.8)),
 ])
 def test_fused_step_equals_staged(S, name, overrides):
-    """seer_decode_step reproduces the four staged calls bit for bit."""
+    """seer_decode_step reproduces the four staged calls bit for bit.  Under
+    threshold and top-p with an automatic split count the fused decode
+    divides all pairs' chunks evenly over the grid (stream-K), which sums in
+    another order: there cache, indices and logits stay bit-identical, both
+    fused calls give the same bits, and every pair matches the oracle."""
     w = WORKLOADS[name].replace(**overrides)
     say(f"fused vs staged {name} {overrides}")
     inp = make_inputs(w, device=DEV)
@@ -812,21 +816,84 @@ def test_fused_step_equals_staged(S, name, overrides):
     b.fused_step(*args)
     c.fused_step(*args, keep_logits=False)  # logits pointer NULL
     torch.cuda.synchronize()
+    stream_k = w.mode != "topk"
     for x in (b, c):
         assert torch.equal(a.kcomp_lens, x.kcomp_lens)
         assert torch.equal(a.kcomp, x.kcomp)
         assert torch.equal(a.num_selected, x.num_selected)
         assert torch.equal(a.block_idx, x.block_idx)
-        assert torch.equal(a.out, x.out)
-        assert torch.equal(a.lse, x.lse)
+        ref = b if stream_k else a
+        assert torch.equal(ref.out, x.out)
+        assert torch.equal(ref.lse, x.lse)
     assert torch.equal(a.logits, b.logits)
     assert bool((c.logits == 123.0).all())  # untouched
     # the fused workspace's split counters (its first B*Hkv ints, present
     # when the decode splits) are left at zero
-    if b.num_split > 1:
+    if b.num_split > 1 or stream_k:
         assert int(b.step_ws[: w.batch * w.num_kv_heads].view(torch.int32).abs().sum()) == 0
-    # one pair against the oracle as well
-    _check_pair(w, inp, b, w.batch - 1, w.num_kv_heads - 1, f"fused {name}")
+    # pairs against the oracle as well: all of them for stream-K
+    pairs = ([(bb, hh) for bb in range(w.batch) for hh in range(w.num_kv_heads)] if stream_k
+             else [(w.batch - 1, w.num_kv_heads - 1)])
+    for bb, hh in pairs:
+        _check_pair(w, inp, b, bb, hh, f"fused {name} b={bb} h={hh}")
+
+
+SK_CASES = [
+    # lengths from 40 to 20000 tokens, threshold: 2 to ~150 blocks per pair
+    ("threshold_b128", dict(batch=5, max_seq_len=20000, seq_len_range=(40, 20000)), None),
+    # one long sequence among short ones: its pairs span many workgroups,
+    # more parts than the merge holds in registers
+    ("qwen3_14b_b16", dict(batch=4, mode="topp", tau=0.97), [32768, 700, 64, 1]),
+    # an empty sequence (no active chunk), a lone partial block, fewer
+    # chunks than workgroups
+    ("tiny", dict(batch=5, mode="threshold", tau=0.02), [0, 37, 1024, 64, 700]),
+    # two pairs on 256 workgroups, one of 2048 blocks: it is cut into more
+    # parts than the merge's weight array holds, so they merge in batches
+    ("qwen3_8b_layer", dict(batch=2, num_q_heads=4, num_kv_heads=1, max_seq_len=131072,
+                            seq_len=131072, mode="topp", tau=0.99), [131072, 64]),
+]
+
+
+@pytest.mark.parametrize("name,overrides,lens", SK_CASES)
+def test_fused_step_stream_k_matches_oracle(S, name, overrides, lens):
+    """The stream-K decode of the fused step (threshold, top-p, automatic
+    split count) on very uneven selections: every pair against the oracle,
+    empty pairs written as 0 and -inf, the same bits from run to run, and the
+    per-pair counters back at zero."""
+    w = WORKLOADS[name].replace(**overrides)
+    say(f"stream-K fused step {name} {overrides} lens={lens}")
+    inp = make_inputs(w, device=DEV)
+    if lens is not None:
+        inp["seq_lens"].copy_(torch.tensor(lens, dtype=torch.int32))
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    st = S.DecodeStep(dims, mode=MODES[w.mode], topk_blocks=w.topk_blocks, threshold=w.tau,
+                      device=DEV)
+    seq = inp["seq_lens"]
+    st.build_cache(inp["k"], inp["w_k"], seq)
+    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    st.out.fill_(7.0)
+    st.lse.fill_(7.0)
+    st.fused_step(*args, keep_logits=False)
+    first = (st.out.clone(), st.lse.clone())
+    st.fused_step(*args, keep_logits=False)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0].view(torch.int16), st.out.view(torch.int16))
+    assert torch.equal(first[1].view(torch.int32), st.lse.view(torch.int32))
+    pairs = w.batch * w.num_kv_heads
+    assert int(st.step_ws[:pairs].view(torch.int32).abs().sum()) == 0
+    nsel = st.num_selected.cpu()
+    assert int(nsel.max()) > 4 * max(int(nsel.min()), 1)  # the selections are uneven
+    g = w.group
+    for bb in range(w.batch):
+        for hh in range(w.num_kv_heads):
+            what = f"stream-K {name} b={bb} h={hh} L={int(seq[bb])} n={int(nsel[bb, hh])}"
+            if int(seq[bb]) == 0:
+                assert int(nsel[bb, hh]) == 0, what
+                assert torch.all(st.out[bb, hh * g:(hh + 1) * g] == 0), what
+                assert torch.all(torch.isneginf(st.lse[bb, hh * g:(hh + 1) * g])), what
+            else:
+                _check_pair(w, inp, st, bb, hh, what)
 
 
 def test_fused_pipeline_steps_match_oracle(S):
