@@ -847,6 +847,9 @@ SK_CASES = [
     # an empty sequence (no active chunk), a lone partial block, fewer
     # chunks than workgroups
     ("tiny", dict(batch=5, mode="threshold", tau=0.02), [0, 37, 1024, 64, 700]),
+    # 16 query heads per KV head: the 4-wave workgroup of the launcher
+    ("qwen3_14b_b16", dict(batch=3, num_q_heads=32, num_kv_heads=2, mode="threshold",
+                           tau=0.01), [32768, 5000, 300]),
     # two pairs on 256 workgroups, one of 2048 blocks: it is cut into more
     # parts than the merge's weight array holds, so they merge in batches
     ("qwen3_8b_layer", dict(batch=2, num_q_heads=4, num_kv_heads=1, max_seq_len=131072,
