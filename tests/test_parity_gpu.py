@@ -1119,3 +1119,32 @@ def test_bound_step_equals_staged(S, num_split, mode):
     pairs = w.batch * w.num_kv_heads
     assert int(fused.step_ws.view(torch.int32)[:pairs].abs().sum()) == 0
     _check_pair(w, inp, fused, 1, 3, "bound step vs oracle")
+
+
+def test_fused_step_split_sized_workspace_skips_stream_k(S):
+    """A fused-step workspace sized for the split decode alone (the size the
+    query returns for an explicit split count) is still accepted under top-p
+    with an automatic split: the step then keeps fixed splits and equals the
+    staged calls bit for bit."""
+    w = WORKLOADS["qwen3_14b_b16"].replace(batch=3, mode="topp", tau=0.9)
+    say("fused step with a split-sized workspace")
+    inp = make_inputs(w, device=DEV)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    kw = dict(mode=MODES["topp"], threshold=w.tau, device=DEV)
+    fused = S.DecodeStep(dims, **kw)
+    staged = S.DecodeStep(dims, **kw)
+    assert fused.split_request == 0 and fused.num_split > 1
+    small = S.seer_decode_step_workspace_bytes(dims, fused.max_selected, fused.num_split)
+    assert small < S.seer_decode_step_workspace_bytes(dims, fused.max_selected, 0)
+    fused.step_ws = torch.zeros((small + 3) // 4, dtype=torch.float32, device=DEV)
+    fused.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    _clone_state(fused, staged)
+    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+            inp["seq_lens"])
+    fused.fused_step(*args)
+    staged.step(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.block_idx, staged.block_idx)
+    assert torch.equal(fused.out.view(torch.int16), staged.out.view(torch.int16))
+    assert torch.equal(fused.lse.view(torch.int32), staged.lse.view(torch.int32))
