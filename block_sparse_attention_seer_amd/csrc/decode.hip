@@ -38,7 +38,14 @@
 //     go around the per-XCD L2, so no release/acquire fence is needed: those
 //     turn into L2 write-back / invalidate on gfx950, which serialise across
 //     workgroups.  Without counters in the workspace a second small kernel
-//     merges the splits instead.
+//     merges the splits instead;
+//   * K rows use ordinary loads and V rows non-temporal ones: every chunk's
+//     scores wait on K, while V is consumed later and need not take Infinity
+//     Cache capacity;
+//   * selections of very different sizes (threshold, top-p) can instead be
+//     divided stream-K: each workgroup takes an equal share of all pairs'
+//     chunks, decodes the pairs in it one after another, and a pair cut
+//     between shares merges through the same counter protocol.
 #include "seer_device.hpp"
 #include "seer_internal.h"
 
