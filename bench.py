@@ -84,6 +84,11 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=24)
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--num-split", type=int, default=0)
+    ap.add_argument("--select", choices=("workload", "topk", "threshold", "topp"),
+                    default="workload",
+                    help="selection rule of the timed steps (default: the workload's own)")
+    ap.add_argument("--mass", type=float, default=0.9,
+                    help="threshold tau or top-p mass p when --select overrides the rule")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flushed-iters", type=int, default=100,
@@ -130,6 +135,8 @@ def main() -> int:
     if args.extra:
         return extra_lines(S, torch, np, dev)
     w = WORKLOADS[args.workload]
+    if args.select != "workload":
+        w = w.replace(mode=args.select, tau=args.mass)
     if w.seq_len is None:
         print("bench.py times single-length workloads (qwen3_8b_layer, qwen3_14b_b16, tiny)",
               file=sys.stderr)
@@ -138,7 +145,7 @@ def main() -> int:
     g = w.group
     L = w.seq_len
     dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
-    mode = S.SELECT_TOPK if w.mode == "topk" else S.SELECT_THRESHOLD
+    mode = {"topk": S.SELECT_TOPK, "threshold": S.SELECT_THRESHOLD, "topp": S.SELECT_TOPP}[w.mode]
 
     # ---- replicas of the inputs, each with its own cache and step buffers
     R = max(1, args.replicas)
@@ -332,7 +339,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "d_gate": dg, "block_size": bs, "seq_len": L, "mode": w.mode,
-                   "topk_blocks": w.topk_blocks, "num_split": reps[0][1].num_split,
+                   **({"topk_blocks": w.topk_blocks} if w.mode == "topk" else {"mass": w.tau}),
+                   "num_split": reps[0][1].num_split,
                    "replicas": R},
         "roofline": {
             "bound": "hbm",
