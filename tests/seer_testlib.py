@@ -39,19 +39,45 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def assert_out_close(o_gpu: np.ndarray, o_ref: np.ndarray, what: str = "") -> float:
+    """Elementwise |o_gpu - o_ref| <= 2e-2 + 1e-2 |o_ref|.  Written as a
+    negated <= so that a NaN or infinite output (an element never written,
+    or poisoned input that leaked through) fails instead of passing."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    assert o_gpu.shape == o_ref.shape, f"{what}: shape {o_gpu.shape} != {o_ref.shape}"
     err = np.abs(o_gpu - o_ref)
     bound = OUT_ATOL + OUT_RTOL * np.abs(o_ref)
-    bad = err > bound
+    bad = ~(err <= bound)
     assert not bad.any(), (
-        f"{what}: {int(bad.sum())} of {bad.size} outputs outside 2e-2 + 1e-2|ref|; "
-        f"max err {err.max():.3e}")
+        f"{what}: {int(bad.sum())} of {bad.size} outputs outside 2e-2 + 1e-2|ref| "
+        f"({int((~np.isfinite(o_gpu)).sum())} not finite); max err {np.nanmax(err):.3e}")
     return float(err.max()) if err.size else 0.0
 
 
 def assert_lse_close(l_gpu: np.ndarray, l_ref: np.ndarray, what: str = "") -> None:
+    """|l_gpu - l_ref| <= 1e-3, with -inf matching -inf (empty selections);
+    NaN fails."""
+    l_gpu = np.asarray(l_gpu, dtype=np.float64)
+    l_ref = np.asarray(l_ref, dtype=np.float64)
+    assert l_gpu.shape == l_ref.shape, f"{what}: shape {l_gpu.shape} != {l_ref.shape}"
     both_inf = np.isneginf(l_gpu) & np.isneginf(l_ref)
-    err = np.abs(np.where(both_inf, 0.0, l_gpu - l_ref))
+    with np.errstate(invalid="ignore"):
+        err = np.abs(np.where(both_inf, 0.0, l_gpu - l_ref))
     assert np.all(err <= LSE_ATOL), f"{what}: lse max err {np.nanmax(err):.3e}"
+
+
+def assert_gt_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> None:
+    """Prefill ground truth: |got - ref| <= 1e-6 + 2e-3 |ref| elementwise
+    (derivation in tests/test_prefill_gpu.py); NaN and inf fail."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
+    err = np.abs(got - ref)
+    bound = 1e-6 + 2e-3 * np.abs(ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} ground-truth values off "
+                           f"({int((~np.isfinite(got)).sum())} not finite), worst "
+                           f"{float(np.nanmax(err - bound)):.3e} over the bound")
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:

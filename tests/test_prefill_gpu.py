@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import oracle as O
-from seer_testlib import assert_lse_close, assert_out_close, f64
+from seer_testlib import assert_gt_close, assert_lse_close, assert_out_close, f64
 from workloads import PREFILL_WORKLOADS, PrefillWorkload, make_prefill_inputs
 
 pytestmark = pytest.mark.gpu
@@ -42,14 +42,6 @@ def S():
     import block_sparse_attention_seer_amd as S
     S.lib()
     return S
-
-
-def assert_gt_close(got, ref, what):
-    err = np.abs(got - ref)
-    bound = 1e-6 + 2e-3 * np.abs(ref)
-    bad = err > bound
-    assert not bad.any(), (f"{what}: {int(bad.sum())} ground-truth values off, worst "
-                           f"{float((err - bound).max()):.3e} over the bound")
 
 
 def run(S, dims, inp, scale, with_gt=True):
