@@ -241,21 +241,41 @@ def _forced_blocks(n_cached: int, seq_len: int, block_size: int) -> list:
     return list(range(n_cached, total))
 
 
+def _keep_within_capacity(ranked_scored: list, forced: list,
+                          capacity: Optional[int]) -> list:
+    """The active set when it may not fit the index row.
+
+    [CP Knowl 5]: the incomplete last block is always selected, so blocks
+    without a cache entry (the partial block, plus complete blocks a lagging
+    cache has not scored yet) come before scored blocks: with a capacity of
+    c, the last min(c, #forced) forced blocks are kept (the partial block is
+    the last), and the scored blocks fill what room is left in their given
+    order (best first for top-k and top-p).
+    """
+    if capacity is None:
+        return list(ranked_scored) + list(forced)
+    cap = max(0, int(capacity))
+    kept_forced = list(forced)[max(0, len(forced) - cap):]
+    room = cap - len(kept_forced)
+    return list(ranked_scored)[:room] + kept_forced
+
+
 def select_topk(z: np.ndarray, k: int, seq_len: int, block_size: int,
                 capacity: Optional[int] = None) -> np.ndarray:
     """Token-budget selection: the k largest logits, plus the forced blocks.
 
     z holds the logits of the cached complete blocks (len = n_cached).  Order
     is (z descending, index ascending), so ties go to the lower block index.
-    Returns ascending block indices, truncated to `capacity` if given.
+    Returns ascending block indices.  With a `capacity`, the forced blocks are
+    kept first and k shrinks to the room left (_keep_within_capacity).
     """
     z = np.asarray(z, dtype=np.float64)
     n = z.shape[0]
     k_eff = max(0, min(int(k), n))
     order = sorted(range(n), key=lambda j: (-z[j], j))
-    chosen = sorted(order[:k_eff]) + _forced_blocks(n, seq_len, block_size)
-    out = np.asarray(sorted(chosen), dtype=np.int64)
-    return out if capacity is None else out[:capacity]
+    chosen = _keep_within_capacity(order[:k_eff], _forced_blocks(n, seq_len, block_size),
+                                   capacity)
+    return np.asarray(sorted(chosen), dtype=np.int64)
 
 
 def select_threshold(z: np.ndarray, tau: float, seq_len: int, block_size: int,
@@ -263,7 +283,9 @@ def select_threshold(z: np.ndarray, tau: float, seq_len: int, block_size: int,
     """Threshold selection: blocks whose softmax score exceeds tau, plus forced.
 
     softmax_j(z) > tau  <=>  z_j > ln(tau) + LSE(z), evaluated in float64.
-    The softmax runs over the scored (complete, cached) blocks only.
+    The softmax runs over the scored (complete, cached) blocks only.  With a
+    `capacity` too small for the set, the forced blocks are kept first and
+    the scored blocks fill the rest in index order (_keep_within_capacity).
     """
     z = np.asarray(z, dtype=np.float64)
     n = z.shape[0]
@@ -273,9 +295,8 @@ def select_threshold(z: np.ndarray, tau: float, seq_len: int, block_size: int,
         lse = m + math.log(float(np.sum(np.exp(z - m))))
         thr = (math.log(tau) if tau > 0 else -math.inf) + lse
         chosen = [j for j in range(n) if z[j] > thr]
-    chosen += _forced_blocks(n, seq_len, block_size)
-    out = np.asarray(sorted(chosen), dtype=np.int64)
-    return out if capacity is None else out[:capacity]
+    chosen = _keep_within_capacity(chosen, _forced_blocks(n, seq_len, block_size), capacity)
+    return np.asarray(sorted(chosen), dtype=np.int64)
 
 
 def select_topp(z: np.ndarray, p: float, seq_len: int, block_size: int,
@@ -304,9 +325,8 @@ def select_topp(z: np.ndarray, p: float, seq_len: int, block_size: int,
                 break
             chosen.append(j)
             mass += float(prob[j])
-    chosen += _forced_blocks(n, seq_len, block_size)
-    out = np.asarray(sorted(chosen), dtype=np.int64)
-    return out if capacity is None else out[:capacity]
+    chosen = _keep_within_capacity(chosen, _forced_blocks(n, seq_len, block_size), capacity)
+    return np.asarray(sorted(chosen), dtype=np.int64)
 
 
 def topk_budget_blocks(token_budget: int, block_size: int) -> int:

@@ -221,6 +221,44 @@ def test_gate_logits_relative_positions_closed_form():
     np.testing.assert_allclose(res["q_gate"], [math.cos(L - 1), math.sin(L - 1)], atol=1e-15)
 
 
+def test_decode_pair_routes_pre_and_post_rope_inputs():
+    """[CP Knowl 1, 2]: the gate scores with the *pre*-RoPE query (and a cache
+    built from pre-RoPE keys), attention uses the model's post-RoPE q and K.
+    Built so that the two queries pick different blocks: q_nope points along
+    e0 and only block 2's pre-RoPE keys do too, while q points along e1 and
+    only block 0's post-RoPE keys do.  With theta huge the gate's own RoPE is
+    the identity at these positions, so the logits have the closed form
+    z_j = <q_nope, mean key of block j> / sqrt(d_gate) (W_k = [0 0 I])."""
+    d, b, L = 4, 4, 16
+    e0, e1 = np.eye(d)[0], np.eye(d)[1]
+    k_nope = np.zeros((L, d))
+    k_nope[2 * b:3 * b] = 2.0 * e0     # block 2 aligned with q_nope
+    k_post = np.zeros((L, d))
+    k_post[0:b] = 5.0 * e1             # block 0 aligned with q
+    v = np.arange(L * d, dtype=np.float64).reshape(L, d)
+    w_k = np.hstack([np.zeros((d, 2 * d)), np.eye(d)])
+    theta = 1e300  # every frequency but the first is 0; the first pair sees cos/sin of pos
+    kc = O.build_kcomp(k_nope, w_k, L, b, theta)
+    q_nope, q = e0[None, :], e1[None, :]
+    res = O.decode_pair(q_nope, q, k_nope, k_post, v, np.eye(d), kc, L, b, mode="topk",
+                        topk=1, theta=theta)
+    # gate: only the pre-RoPE inputs count; frequency 0 rotates pair (0, 2)
+    # by pos, so z_j = 2 cos((L-1) - j b) / 2 for block 2 and 0 elsewhere
+    expect = np.zeros(L // b)
+    expect[2] = 2.0 * math.cos((L - 1) - 2 * b) / math.sqrt(d)
+    np.testing.assert_allclose(res["logits"], expect, atol=2 ** -7)
+    assert res["blocks"].tolist() == [2]
+    # attention: q over the post-RoPE keys of block 2 (all zero scores),
+    # so the output is the mean of block 2's values
+    np.testing.assert_allclose(res["o"][0], v[2 * b:3 * b].mean(axis=0), atol=1e-12)
+    np.testing.assert_allclose(res["lse"][0], math.log(b), atol=1e-12)
+    # swapping the roles changes both the selection and the output
+    kc_swapped = O.build_kcomp(k_post, w_k, L, b, theta)
+    swapped = O.decode_pair(q, q_nope, k_post, k_nope, v, np.eye(d), kc_swapped, L, b,
+                            mode="topk", topk=1, theta=theta)
+    assert swapped["blocks"].tolist() == [0]
+
+
 # --------------------------------------------------------------- selection
 
 def test_topk_matches_brute_force_subsets():
@@ -245,7 +283,44 @@ def test_topk_ties_budget_and_partial_block():
     assert list(O.select_topk(z, 0, 5 * b, b)) == []
     assert list(O.select_topk(z, 2, 5 * b + 3, b)) == [1, 2, 5]  # partial block 5 forced
     assert list(O.select_topk(np.zeros(0), 4, 37, b)) == [0]     # L < b: only the partial
-    assert list(O.select_topk(z, 2, 5 * b + 3, b, capacity=2)) == [1, 2]
+    # a row too short for k + forced: the forced partial block stays, k shrinks
+    assert list(O.select_topk(z, 2, 5 * b + 3, b, capacity=2)) == [1, 5]
+
+
+def test_capacity_keeps_forced_blocks_first():
+    """[CP Knowl 5]: the incomplete last block is always selected.  With a
+    cache that lags (complete blocks not yet scored, so more than one forced
+    block) and an index row of k + 1, the forced blocks are kept and the
+    scored part is the best subset that fits, by brute force over subsets."""
+    rng = np.random.default_rng(21)
+    b = 16
+    for trial in range(40):
+        n_cached = int(rng.integers(3, 10))
+        lag = int(rng.integers(1, 3))              # complete blocks not yet cached
+        L = (n_cached + lag) * b + int(rng.integers(1, b))  # ... plus a partial block
+        forced = list(range(n_cached, n_cached + lag + 1))
+        z = rng.normal(size=n_cached)
+        k = int(rng.integers(1, n_cached))
+        cap = k + 1
+        for mode, got in (("topk", O.select_topk(z, k, L, b, capacity=cap)),
+                          ("threshold", O.select_threshold(z, 0.0, L, b, capacity=cap)),
+                          ("topp", O.select_topp(z, 1.0, L, b, capacity=cap))):
+            got = list(got)
+            assert len(got) == min(cap, n_cached + len(forced)), mode
+            assert got[-1] == n_cached + lag, mode          # the partial block
+            kept_forced = forced[max(0, len(forced) - cap):]
+            assert [j for j in got if j >= n_cached] == kept_forced, mode
+            room = cap - len(kept_forced)
+            scored = [j for j in got if j < n_cached]
+            if mode == "threshold":  # tau = 0 passes all: lowest indices fill the room
+                assert scored == list(range(min(room, n_cached))), mode
+            else:                    # top-k, and top-p at p = 1: the best `room`
+                best = max(itertools.combinations(range(n_cached), room),
+                           key=lambda s_: sum(z[list(s_)])) if room > 0 else ()
+                assert scored == sorted(best), mode
+    # more forced blocks than the row holds: the last ones, ending in the partial block
+    z = np.array([3.0, 1.0])
+    assert list(O.select_topk(z, 1, 6 * b + 5, b, capacity=2)) == [5, 6]
 
 
 def test_threshold_matches_explicit_softmax():
