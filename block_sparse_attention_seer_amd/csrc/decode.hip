@@ -37,8 +37,7 @@
 //     loads), writes the output and resets the counter.  Coherent accesses
 //     go around the per-XCD L2, so no release/acquire fence is needed: those
 //     turn into L2 write-back / invalidate on gfx950, which serialise across
-//     workgroups.  Without counters in the workspace a second small kernel
-//     merges the splits instead;
+//     workgroups;
 //   * K rows use ordinary loads and V rows non-temporal ones: every chunk's
 //     scores wait on K, while V is consumed later and need not take Infinity
 //     Cache capacity;
@@ -69,7 +68,7 @@ struct DecodeParams {
   const int32_t* seq_lens;
   const int32_t* block_idx;
   const int32_t* num_selected;
-  int32_t* counters;  // [pairs] finished splits (merge in the decode launch), or null
+  int32_t* counters;  // [pairs] finished splits of each pair (zero between launches)
   float* part_lse;  // [pairs, S, G]   log2-domain lse of each split
   float* part_o;    // [pairs, S, G, D] normalised split outputs
   uint16_t* out;
@@ -359,9 +358,6 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
       p.out[(out_base + head) * D + dim] = f2bf(o);
       if (dim == 0 && p.lse != nullptr)
         p.lse[out_base + head] = any ? (M + fast_log2(lsum)) * kLn2 : -INFINITY;
-    } else if (p.counters == nullptr) {
-      p.part_o[(part * G + head) * D + dim] = o;
-      if (dim == 0) p.part_lse[part * G + head] = any ? M + fast_log2(lsum) : -INFINITY;
     } else {
       // device-coherent stores (they write through the per-XCD L2)
       __hip_atomic_store(&p.part_o[(part * G + head) * D + dim], o, __ATOMIC_RELAXED,
@@ -371,7 +367,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (pt.nparts == 1 || p.counters == nullptr) return;
+  if (pt.nparts == 1) return;
 
   // ---- the last split of this (b, h) to finish merges all splits.
   // Partials travel only through device-coherent stores and loads, so the
@@ -652,74 +648,6 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge of the splits of one (b, h): o = sum_s w_s o_s with
-// w_s = exp2(lse_s - M) / sum_s' exp2(lse_s' - M).  Each thread first issues
-// the loads of all its split outputs (independent of the weights), then the
-// lse values are reduced while those loads are in flight.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineMaxS = 8;  // split outputs held in registers per pass
-
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p) {
-  __shared__ float sm_w[kMaxSplit * 16];
-  __shared__ float sm_lse[16];
-  const int pair = blockIdx.x;
-  const int S = p.num_split;
-  const int G = p.G;
-  const int b = pair / p.Hkv;
-  const int h = pair - b * p.Hkv;
-  const int tid = threadIdx.x;
-  const float* plse = p.part_lse + static_cast<int64_t>(pair) * S * G;
-  const float* po = p.part_o + static_cast<int64_t>(pair) * S * G * D;
-  const int64_t out_base = static_cast<int64_t>(b) * p.Hq + h * G;
-  const int nel = G * D;
-
-  // element e = tid + 256 i (i < 4 covers G*D <= 16*64; D=128 needs i < 8)
-  constexpr int EPT = 16 * D / kCombineThreads;
-  float pre[EPT][kCombineMaxS];
-  const int s_pre = min(S, kCombineMaxS);
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int e = tid + kCombineThreads * i;
-    const int head = e / D;
-#pragma unroll
-    for (int s = 0; s < kCombineMaxS; ++s)
-      pre[i][s] = (e < nel && s < s_pre) ? po[(s * G + head) * D + (e - head * D)] : 0.f;
-  }
-  for (int i = tid; i < S * G; i += kCombineThreads) sm_w[i] = plse[i];
-  __syncthreads();
-  if (tid < G) {
-    const int head = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, sm_w[s * G + head]);
-    float tot = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ls = sm_w[s * G + head];
-      const float f = (M == -INFINITY || ls == -INFINITY) ? 0.f : fast_exp2(ls - M);
-      sm_w[s * G + head] = f;
-      tot += f;
-    }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    for (int s = 0; s < S; ++s) sm_w[s * G + head] *= inv;
-    sm_lse[head] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int e = tid + kCombineThreads * i;
-    if (e >= nel) break;
-    const int head = e / D;
-    const int dim = e - head * D;
-    float o = 0.f;
-#pragma unroll
-    for (int s = 0; s < kCombineMaxS; ++s)
-      if (s < s_pre) o += sm_w[s * G + head] * pre[i][s];
-    for (int s = kCombineMaxS; s < S; ++s) o += sm_w[s * G + head] * po[(s * G + head) * D + dim];
-    p.out[(out_base + head) * D + dim] = f2bf(o);
-    if (dim == 0 && p.lse != nullptr) p.lse[out_base + head] = sm_lse[head];
-  }
-}
-
 template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK = false>
 void launch_one(const DecodeParams& p, int grid, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(NW) * p.G * D * sizeof(float);
@@ -787,16 +715,12 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   p.num_pages = a.num_pages;
   p.page_stride = a.page_stride;
   p.page_head_stride = a.page_head_stride;
-  const bool inline_merge = a.merge_inline;
   const bool dense = (a.block_idx == nullptr);
   const bool paged = a.block_table != nullptr;
-  const int wpg = a.waves_per_group;
-  const int nw = ((wpg == 4 || wpg == 8) && decode_waves_fit(wpg, G, d.head_dim))
-                     ? wpg
-                     : decode_waves_per_group(G, d.head_dim);
-  // stream-K where it applies: a selection over a contiguous cache, merged in
-  // the launch, with the pairs' prefix and the wave merge both in LDS
-  const bool sk = a.stream_k && !dense && !paged && inline_merge && pairs <= kSkMaxPairs &&
+  const int nw = decode_waves_per_group(G, d.head_dim);
+  // stream-K where it applies: a selection over a contiguous cache, with the
+  // pairs' prefix and the wave merge both in LDS
+  const bool sk = a.stream_k && !dense && !paged && pairs <= kSkMaxPairs &&
                   static_cast<int64_t>(nw) * G * d.head_dim * 4 <= kSkMergeLds;
   if (S > 1 || sk) {
     char* ws = static_cast<char*>(a.workspace);
@@ -805,7 +729,7 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
     // stream-K: two partial slots per workgroup
     size_t lbytes = static_cast<size_t>(pairs) * S * (sk ? 2 : 1) * G * sizeof(float);
     lbytes = (lbytes + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
-    p.counters = inline_merge ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    p.counters = reinterpret_cast<int32_t*>(ws);
     p.part_lse = reinterpret_cast<float*>(ws + cbytes);
     p.part_o = reinterpret_cast<float*>(ws + cbytes + lbytes);
   }
@@ -823,21 +747,10 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
     paged ? launch_variant<8, true>(key, p, grid, s) : launch_variant<8, false>(key, p, grid, s);
   else
     paged ? launch_variant<4, true>(key, p, grid, s) : launch_variant<4, false>(key, p, grid, s);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error(std::string("decode launch: ") + hipGetErrorString(e));
     return SEER_ERR_HIP;
-  }
-  if (S > 1 && !inline_merge && !sk) {
-    if (d.head_dim == 128)
-      hipLaunchKernelGGL(combine_kernel<128>, dim3(grid64 / S), dim3(kCombineThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(combine_kernel<64>, dim3(grid64 / S), dim3(kCombineThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) {
-      set_error(std::string("combine launch: ") + hipGetErrorString(e));
-      return SEER_ERR_HIP;
-    }
   }
   return SEER_OK;
 }

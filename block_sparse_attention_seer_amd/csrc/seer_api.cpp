@@ -3,7 +3,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <string>
 
 #include "seer_internal.h"
@@ -25,28 +24,6 @@ int fail(int code, const std::string& why) {
     int rc_ = call;                          \
     if (rc_ != SEER_OK) return fail(rc_, why_); \
   } while (0)
-
-// Optional override of the decode kernel's waves per workgroup (4 or 8),
-// read once from SEER_DECODE_WAVES; 0 = automatic.  A tuning knob only.
-int tuning_waves() {
-  static const int v = [] {
-    const char* e = std::getenv("SEER_DECODE_WAVES");
-    const int x = e ? std::atoi(e) : 0;
-    return (x == 4 || x == 8) ? x : 0;
-  }();
-  return v;
-}
-
-// Optional choice of where the splits are merged, read once from
-// SEER_DECODE_MERGE ("kernel" = a second launch); default: in the decode
-// launch.  A tuning knob only.
-bool tuning_merge_inline() {
-  static const bool v = [] {
-    const char* e = std::getenv("SEER_DECODE_MERGE");
-    return !(e && std::string(e) == "kernel");
-  }();
-  return v;
-}
 
 int check_select_args(const seer_dims* dims, int32_t mode, int32_t topk_blocks, float threshold,
                       int32_t max_selected) {
@@ -253,8 +230,7 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
     SEER_CHECK(check_ptr(workspace, 256, "workspace", &why_));
   }
   seer::DecodeArgs a{q, k, v, seq_lens, block_idx, num_selected, max_blocks, scale, s,
-                     tuning_waves(), tuning_merge_inline(), workspace, out, lse,
-                     commit_lens, commit_max_new};
+                     workspace, out, lse, commit_lens, commit_max_new};
   a.stream_k = stream_k;
   if (paged != nullptr) {
     SEER_CHECK(check_paged(dims, *paged, &why_));

@@ -109,9 +109,7 @@ struct DecodeArgs {
   int max_selected;             // index row length (sparse)
   float scale;
   int num_split;
-  int waves_per_group;          // 0 = automatic (8 or 4)
-  bool merge_inline;            // merge splits in the decode launch (counters in the workspace)
-  void* workspace;
+  void* workspace;              // split counters and partials (num_split > 1 or stream-K)
   uint16_t* out;
   float* lse;
   int32_t* commit_lens;         // fused step: raise kcomp_lens here (or nullptr)

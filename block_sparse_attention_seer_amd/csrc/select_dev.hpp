@@ -270,6 +270,14 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
   const int j1 = min(nc, j0 + vpt);
   const KeyRange<KPL> kr(keys, j0, j1 - j0);
 
+  // Blocks without a cache entry (normally just the partial block) are
+  // always active ([CP Knowl 5]).  They come first when the row is short:
+  // the last min(forced, max_sel) of them are kept, and the scored blocks
+  // get the room left (top-k's k shrinks to it).
+  const int forced = max(0, total_blocks - nc);
+  const int kept_forced = min(forced, max_sel);
+  const int room = max_sel - kept_forced;
+
   // A key is taken iff  key > lo, or key == lo and (whole || rank < need)
   // (top-k), or z > thr (threshold); `all` / `none` short-cut both.
   bool all = false, none = false, whole = true;
@@ -278,7 +286,7 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
   float thr = 0.f;
 
   if (mode == SEER_SELECT_TOPK) {
-    const int k = min(topk, nc);
+    const int k = min(min(topk, nc), room);
     if (k >= nc) {
       all = true;
     } else if (k <= 0) {
@@ -501,18 +509,17 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
     int rank = eq_before;
     kr.each([&](int j, float z) {
       if (taken(z, rank)) {
-        if (pos < max_sel) out[pos] = j;
+        if (pos < room) out[pos] = j;
         ++pos;
       }
     });
   }
-  // blocks without a cache entry (normally the partial block) are forced
-  const int forced = max(0, total_blocks - nc);
-  for (int f = tid; f < forced; f += NT) {
-    const int p = scored_total + f;
-    if (p < max_sel) out[p] = nc + f;
-  }
-  const int written = min(scored_total + forced, max_sel);
+  // then the forced blocks (top-k fits them by construction; threshold and
+  // top-p rows hold every block, so nothing scored is cut there)
+  const int scored_written = min(scored_total, room);
+  const int f0 = total_blocks - kept_forced;
+  for (int f = tid; f < kept_forced; f += NT) out[scored_written + f] = f0 + f;
+  const int written = scored_written + kept_forced;
   for (int i = written + tid; i < max_sel; i += NT) out[i] = -1;
   if (tid == 0) *count_out = written;
 }

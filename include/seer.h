@@ -171,8 +171,10 @@ int seer_gate_scores(const seer_dims* dims, const uint16_t* q_nope,
  *              no scored block; a p the total does not reach selects all.
  * plus every block in [n_c, N) (normally only the partial block).  Indices
  * are written ascending, -1 after the last; num_selected gets the count.
- * If more than max_selected blocks qualify (only when the cache lags), the
- * lowest max_selected are kept.
+ * The blocks of [n_c, N) come first when the row is short (possible only in
+ * TOPK, when the cache lags so that more than one block is unscored): the
+ * last min(N - n_c, max_selected) of them are kept -- the partial block is
+ * always among them -- and k shrinks to the room left in the row.
  *
  *   mode            SEER_SELECT_TOPK (uses topk_blocks >= 0),
  *                   SEER_SELECT_THRESHOLD (uses 0 <= threshold <= 1) or

@@ -87,6 +87,8 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def host_inputs(inp: dict, w, b: int, h: int, seq_len: int):
+    """Attention's inputs of pair (b, h) in float64: q [g, d], K, V [L, d],
+    and the gate weights W_q[h], W_k[h]."""
     g = w.group
     q = f64(inp["q"][b, h * g:(h + 1) * g])
     k = f64(inp["k"][b, h, :seq_len])
@@ -96,11 +98,24 @@ def host_inputs(inp: dict, w, b: int, h: int, seq_len: int):
     return q, k, v, wq, wk
 
 
+def host_gate_inputs(inp: dict, w, b: int, h: int, seq_len: int):
+    """The gate's pre-RoPE inputs of pair (b, h) in float64: q_nope [g, d]
+    and K_nope [L, d] (the same values as q and K when the inputs were drawn
+    without separate pre-RoPE tensors)."""
+    g = w.group
+    qn = inp.get("q_nope", inp["q"])
+    kn = inp.get("k_nope", inp["k"])
+    return f64(qn[b, h * g:(h + 1) * g]), f64(kn[b, h, :seq_len])
+
+
 def oracle_chain(inp: dict, w, b: int, h: int, seq_len: int, capacity=None):
-    """The oracle's whole decode step for pair (b, h): own cache, gate, selection, attention."""
+    """The oracle's whole decode step for pair (b, h): its own cache built
+    from K_nope, the gate on q_nope, the selection, and attention of q over
+    K and V."""
     q, k, v, wq, wk = host_inputs(inp, w, b, h, seq_len)
-    kc = O.build_kcomp(k, wk, seq_len, w.block_size, w.theta)
-    res = O.decode_pair(q, q, k, k, v, wq, kc, seq_len, w.block_size, mode=w.mode,
+    q_nope, k_nope = host_gate_inputs(inp, w, b, h, seq_len)
+    kc = O.build_kcomp(k_nope, wk, seq_len, w.block_size, w.theta)
+    res = O.decode_pair(q_nope, q, k_nope, k, v, wq, kc, seq_len, w.block_size, mode=w.mode,
                         topk=w.topk_blocks, tau=w.tau, scale=1.0 / math.sqrt(w.head_dim),
                         theta=w.theta, capacity=capacity)
     res["kcomp"] = kc

@@ -396,6 +396,25 @@ def test_paged_decode_equals_contiguous(S, d, bs, Hq, Hkv, lens, table_pad):
             op, lp = res["paged_" + kind]
             assert torch.equal(oc.view(torch.int16), op.view(torch.int16)), f"{kind} out split={ns}"
             assert torch.equal(lc.view(torch.int32), lp.view(torch.int32)), f"{kind} lse split={ns}"
+        # the paged outputs against the oracle ([CP Knowl 14]: the pages only
+        # name PagedAttention; the attention itself is that of [CP Knowl 6])
+        g = Hq // Hkv
+        for kind in ("sparse", "dense"):
+            og, lg = f64(res["paged_" + kind][0]), f64(res["paged_" + kind][1])
+            for b in range(B):
+                kk_all, vv_all = f64(k[b, :, :lens[b]]), f64(v[b, :, :lens[b]])
+                for h in range(Hkv):
+                    qq = f64(q[b, h * g:(h + 1) * g])
+                    if kind == "sparse":
+                        blocks = idx[b, h, :nsel[b, h]].tolist()
+                        o_ref, l_ref = O.sparse_decode_pair(qq, kk_all[h], vv_all[h], lens[b],
+                                                            blocks, bs, scale)
+                    else:
+                        o_ref, l_ref = O.dense_decode_pair(qq, kk_all[h], vv_all[h], lens[b],
+                                                           scale)
+                    what = f"paged {kind} b={b} h={h} split={ns}"
+                    assert_out_close(og[b, h * g:(h + 1) * g], o_ref, what)
+                    assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, what)
 
 
 def test_paged_decode_skips_missing_pages(S):
@@ -576,11 +595,17 @@ def _run_select(S, dims, z, kl, seq, mode, k, tau, max_sel):
     return idx.cpu().numpy(), ns.cpu().numpy()
 
 
+@pytest.mark.parametrize("slack", [3, 1])
 @pytest.mark.parametrize("nbm,bs,k,quant", [(16, 64, 4, None), (512, 64, 64, None),
                                             (512, 64, 52, 0.25), (2048, 64, 64, None),
                                             (300, 128, 7, 1.0), (8192, 64, 100, None)])
-def test_select_topk_exact(S, nbm, bs, k, quant):
-    say(f"select topk nbm={nbm} k={k} quant={quant}")
+def test_select_topk_exact(S, nbm, bs, k, quant, slack):
+    """Top-k on identical logits, bit-exact against the oracle.  Sequence 2's
+    cache lags by six blocks (seven forced blocks): with an index row of
+    k + 1 (the smallest the ABI allows) the forced blocks -- the partial
+    block last -- are kept and k shrinks to the room left, or, when even the
+    forced blocks do not fit, the last of them are kept."""
+    say(f"select topk nbm={nbm} k={k} quant={quant} slack={slack}")
     B, Hkv = 5, 3
     lmax = nbm * bs
     rng = np.random.default_rng(nbm + k)
@@ -591,9 +616,9 @@ def test_select_topk_exact(S, nbm, bs, k, quant):
     z[1, 1, :] = 0.0
     z[0, 1, 7] = 1e30  # one far outlier: the rest share a few value buckets
     z[0, 2, :] = 2.0 ** -(np.arange(nbm) % 140)  # geometric, with exact repeats
-    seq = [lmax, lmax - 5, 3 * bs + 1, bs - 1, 2 * bs]
-    kl = [lmax // bs, (lmax - 5) // bs, 1, 0, 2]  # sequence 2: cache lags by two blocks
-    max_sel = min(k + 3, nbm)
+    seq = [lmax, lmax - 5, 7 * bs + 1, bs - 1, 2 * bs]
+    kl = [lmax // bs, (lmax - 5) // bs, 1, 0, 2]  # sequence 2: cache lags by six blocks
+    max_sel = min(k + slack, nbm)
     dims = S.make_dims(B, 8 * Hkv, Hkv, 128, 128, bs, lmax)
     idx, ns = _run_select(S, dims, z, kl, seq, S.SELECT_TOPK, k, 0.0, max_sel)
     for b in range(B):
@@ -603,6 +628,8 @@ def test_select_topk_exact(S, nbm, bs, k, quant):
             got = idx[b, h, :ns[b, h]]
             assert got.tolist() == ref.tolist(), f"b={b} h={h}"
             assert np.all(idx[b, h, ns[b, h]:] == -1)
+            if seq[b] % bs:  # the partial block is always in the row
+                assert int(got[-1]) == seq[b] // bs, f"b={b} h={h}"
 
 
 @pytest.mark.parametrize("nbm,bs,tau", [(512, 128, 0.01), (64, 64, 0.05), (2048, 64, 0.001),
@@ -672,8 +699,8 @@ def _run_workload_step(S, w, inp, num_split=0):
     seq = inp["seq_lens"]
     # the cache already holds every complete block but the last, which this
     # step's update appends (the step that completes a block)
-    st.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
-    out, lse = st.step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    st.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    out, lse = st.step(inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
     torch.cuda.synchronize()
     return st, out, lse
 
@@ -709,7 +736,7 @@ def test_end_to_end_tiny(S):
     for L in [1024, 1000, 63, 1, 64, 65]:
         say(f"e2e tiny L={L}")
         inp = {kk: (vv.to(DEV) if torch.is_tensor(vv) else vv)
-               for kk, vv in make_inputs(w.replace(seq_len=L)).items()}
+               for kk, vv in make_inputs(w.replace(seq_len=L), separate_nope=True).items()}
         st, out, lse = _run_workload_step(S, w, inp)
         _check_pair(w, inp, st, 0, 0, f"tiny L={L}")
 
@@ -719,7 +746,7 @@ def test_end_to_end_tiny(S):
 def test_end_to_end_full_size_sampled(S, name, pairs):
     w = WORKLOADS[name]
     say(f"e2e full size {name}: generating inputs")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     st, out, lse = _run_workload_step(S, w, inp)
     say(f"e2e full size {name}: checking")
     all_pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
@@ -739,15 +766,15 @@ def test_pipeline_steps_match_oracle(S):
     from workloads import append_token
     w = WORKLOADS["pipeline_128k"].replace(batch=3, max_seq_len=4096, seq_len_range=(300, 700),
                                            steps=70)
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
-    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    st.build_cache(inp["k_nope"], inp["w_k"], inp["seq_lens"])
     gen = torch.Generator(device=DEV).manual_seed(77)
     for step in range(w.steps):
         append_token(inp, gen)
-        st.step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+        st.step(inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
                 inp["seq_lens"])
         if step % 23 == 0 or step == w.steps - 1:
             torch.cuda.synchronize()
@@ -798,7 +825,7 @@ def test_fused_step_equals_staged(S, name, overrides):
     fused calls give the same bits, and every pair matches the oracle."""
     w = WORKLOADS[name].replace(**overrides)
     say(f"fused vs staged {name} {overrides}")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     mode = MODES[w.mode]
@@ -807,11 +834,11 @@ def test_fused_step_equals_staged(S, name, overrides):
     c = S.DecodeStep(dims, mode=mode, topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
     assert a.mode == MODES[w.mode]
     seq = inp["seq_lens"]
-    a.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    a.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - 1, min=0))
     _clone_state(a, b)
     _clone_state(a, c)
     c.logits.fill_(123.0)
-    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
     a.step(*args)
     b.fused_step(*args)
     c.fused_step(*args, keep_logits=False)  # logits pointer NULL
@@ -865,7 +892,7 @@ def test_fused_step_stream_k_matches_oracle(S, name, overrides, lens):
     per-pair counters back at zero."""
     w = WORKLOADS[name].replace(**overrides)
     say(f"stream-K fused step {name} {overrides} lens={lens}")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     if lens is not None:
         inp["seq_lens"].copy_(torch.tensor(lens, dtype=torch.int32))
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
@@ -873,8 +900,8 @@ def test_fused_step_stream_k_matches_oracle(S, name, overrides, lens):
     st = S.DecodeStep(dims, mode=MODES[w.mode], topk_blocks=w.topk_blocks, threshold=w.tau,
                       device=DEV)
     seq = inp["seq_lens"]
-    st.build_cache(inp["k"], inp["w_k"], seq)
-    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    st.build_cache(inp["k_nope"], inp["w_k"], seq)
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
     st.out.fill_(7.0)
     st.lse.fill_(7.0)
     st.fused_step(*args, keep_logits=False)
@@ -904,15 +931,15 @@ def test_fused_pipeline_steps_match_oracle(S):
     from workloads import append_token
     w = WORKLOADS["pipeline_128k"].replace(batch=3, max_seq_len=4096, seq_len_range=(300, 700),
                                            steps=70)
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
-    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    st.build_cache(inp["k_nope"], inp["w_k"], inp["seq_lens"])
     gen = torch.Generator(device=DEV).manual_seed(78)
     for step in range(w.steps):
         append_token(inp, gen)
-        st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+        st.fused_step(inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
                       inp["seq_lens"])
         if step % 23 == 0 or step == w.steps - 1:
             torch.cuda.synchronize()
@@ -931,13 +958,13 @@ def test_fused_step_full_size_sampled(S, name, pairs):
     and workgroup choices, logits not kept) at the workload's full size."""
     w = WORKLOADS[name]
     say(f"fused full size {name}: generating inputs")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
     seq = inp["seq_lens"]
-    st.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
-    st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq,
+    st.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    st.fused_step(inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq,
                   keep_logits=False)
     torch.cuda.synchronize()
     say(f"fused full size {name}: checking")
@@ -962,13 +989,13 @@ def test_fused_step_threshold_full_size_sampled(S):
     within the capacity, and each row's partial block present."""
     w = WORKLOADS["threshold_b128"]
     say("fused full size threshold_b128: generating inputs")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     st = S.DecodeStep(dims, mode=S.SELECT_THRESHOLD, threshold=w.tau, device=DEV)
     seq = inp["seq_lens"]
-    st.build_cache(inp["k"], inp["w_k"], torch.clamp(seq - 1, min=0))
-    st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq,
+    st.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    st.fused_step(inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq,
                   keep_logits=False)
     torch.cuda.synchronize()
     say("fused full size threshold_b128: checking")
@@ -1003,16 +1030,16 @@ def test_pipeline_full_size_sampled(S):
     w = WORKLOADS["pipeline_128k"]
     steps = 3
     say("pipeline full size: generating inputs")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
-    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    st.build_cache(inp["k_nope"], inp["w_k"], inp["seq_lens"])
     start = inp["seq_lens"].cpu().clone()
     gen = torch.Generator(device=DEV).manual_seed(79)
     for step in range(steps):
         append_token(inp, gen)
-        st.fused_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+        st.fused_step(inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
                       inp["seq_lens"], keep_logits=False)
     torch.cuda.synchronize()
     say("pipeline full size: checking")
@@ -1038,7 +1065,7 @@ def test_graph_replays_equal_eager_steps(S, num_split):
     with the automatic split and with two splits."""
     from workloads import append_token
     w = WORKLOADS["pipeline_128k"].replace(batch=4, max_seq_len=4096, seq_len_range=(700, 900))
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     say(f"graph replay, split {num_split}")
@@ -1046,10 +1073,10 @@ def test_graph_replays_equal_eager_steps(S, num_split):
                          num_split=num_split, device=DEV)
     graphed = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks,
                            num_split=num_split, device=DEV)
-    eager.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    eager.build_cache(inp["k_nope"], inp["w_k"], inp["seq_lens"])
     _clone_state(eager, graphed)
     other = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=DEV)
-    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
             inp["seq_lens"])
     graph = graphed.capture_step(*args)
     eager.fused_step(*args, keep_logits=False)
@@ -1084,7 +1111,7 @@ def test_bound_step_equals_staged(S, num_split, mode):
     tau = {"topk": 0.0, "threshold": 0.01, "topp": 0.9}[mode]
     w = WORKLOADS["pipeline_128k"].replace(batch=3, max_seq_len=4096, seq_len_range=(1200, 1300),
                                            mode=mode, tau=tau)
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     say(f"bound step split={num_split} mode={mode}")
@@ -1092,9 +1119,9 @@ def test_bound_step_equals_staged(S, num_split, mode):
               device=DEV)
     fused = S.DecodeStep(dims, **kw)
     staged = S.DecodeStep(dims, **kw)
-    fused.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    fused.build_cache(inp["k_nope"], inp["w_k"], inp["seq_lens"])
     _clone_state(fused, staged)
-    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
             inp["seq_lens"])
     run = fused.bind_step(*args, keep_logits=True)
     gen = torch.Generator(device=DEV).manual_seed(81)
@@ -1128,7 +1155,7 @@ def test_fused_step_split_sized_workspace_skips_stream_k(S):
     staged calls bit for bit."""
     w = WORKLOADS["qwen3_14b_b16"].replace(batch=3, mode="topp", tau=0.9)
     say("fused step with a split-sized workspace")
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, separate_nope=True)
     dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
                        w.block_size, w.max_seq_len)
     kw = dict(mode=MODES["topp"], threshold=w.tau, device=DEV)
@@ -1138,9 +1165,9 @@ def test_fused_step_split_sized_workspace_skips_stream_k(S):
     small = S.seer_decode_step_workspace_bytes(dims, fused.max_selected, fused.num_split)
     assert small < S.seer_decode_step_workspace_bytes(dims, fused.max_selected, 0)
     fused.step_ws = torch.zeros((small + 3) // 4, dtype=torch.float32, device=DEV)
-    fused.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    fused.build_cache(inp["k_nope"], inp["w_k"], inp["seq_lens"])
     _clone_state(fused, staged)
-    args = (inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
             inp["seq_lens"])
     fused.fused_step(*args)
     staged.step(*args)

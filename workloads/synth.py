@@ -10,7 +10,10 @@ Recipe (shared by every workload):
     then rounded to bf16 (round to nearest even);
   * query, keys and values ~ N(0, 1); the model's own RoPE is taken as the
     identity, so the post-RoPE tensors equal the pre-RoPE ones (q = q_nope,
-    K = K_nope);
+    K = K_nope).  With separate_nope=True the pre-RoPE query and keys the
+    gate reads are drawn on their own instead (after every other draw, so
+    the other tensors are unchanged): a model whose RoPE is not the
+    identity, in which the gate's inputs and attention's inputs differ;
   * gate weights ~ N(0, 1/fan_in): W_q[h] is [d_gate, g*d], W_k[h] is
     [d_gate, 3d];
   * "planted" blocks: for each (sequence, KV head) a few complete blocks are
@@ -195,13 +198,15 @@ def _normal_bf16(shape, gen, device, std=1.0) -> torch.Tensor:
 
 
 def make_inputs(w: Workload, device: str = "cpu", seq_lens: Optional[torch.Tensor] = None,
-                kv_len: Optional[int] = None) -> dict:
+                kv_len: Optional[int] = None, separate_nope: bool = False) -> dict:
     """Draw every input tensor of one decode step of workload w.
 
     Returns a dict of tensors on `device`:
-      q [B, Hq, d] bf16 (also the pre-RoPE q_nope), k, v [B, Hkv, Lmax, d]
-      bf16 (k is also K_nope), w_q [Hkv, dg, g*d], w_k [Hkv, dg, 3d] bf16,
-      seq_lens [B] int32, planted [B, Hkv, planted] int64 (block ids).
+      q [B, Hq, d] bf16, k, v [B, Hkv, Lmax, d] bf16 (attention's inputs),
+      q_nope [B, Hq, d], k_nope [B, Hkv, Lmax, d] bf16 (the gate's pre-RoPE
+      inputs: the same tensors as q and k unless separate_nope),
+      w_q [Hkv, dg, g*d], w_k [Hkv, dg, 3d] bf16, seq_lens [B] int32,
+      planted [B, Hkv, planted] int64 (block ids).
     kv_len overrides the allocated cache length (default w.max_seq_len).
     """
     cpu_gen = torch.Generator(device="cpu").manual_seed(w.seed)
@@ -236,15 +241,24 @@ def make_inputs(w: Workload, device: str = "cpu", seq_lens: Optional[torch.Tenso
                     lo, hi = j * w.block_size, (j + 1) * w.block_size
                     blk = k[b, h, lo:hi].float() + 3.0 * u[b, h][None, :]
                     k[b, h, lo:hi] = blk.to(torch.bfloat16)
-    return dict(q=q, k=k, v=v, w_q=w_q, w_k=w_k, seq_lens=seq_lens.to(device),
-                planted=planted)
+    q_nope, k_nope = q, k
+    if separate_nope:
+        q_nope = _normal_bf16((B, Hq, d), dev_gen, device)
+        k_nope = torch.empty((B, Hkv, lmax, d), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            k_nope[b] = _normal_bf16((Hkv, lmax, d), dev_gen, device)
+    return dict(q=q, k=k, v=v, q_nope=q_nope, k_nope=k_nope, w_q=w_q, w_k=w_k,
+                seq_lens=seq_lens.to(device), planted=planted)
 
 
 def append_token(inputs: dict, gen: torch.Generator) -> None:
     """Pipeline step input: draw the new token's q, K, V at position L_b.
 
     Writes K[b, :, L_b] and V[b, :, L_b] for every sequence, redraws q, then
-    increments seq_lens.  Lengths must stay below the cache capacity.
+    increments seq_lens.  Where the gate's pre-RoPE inputs are tensors of
+    their own (make_inputs(separate_nope=True)), K_nope[b, :, L_b] and q_nope
+    are drawn too, after the others.  Lengths must stay below the cache
+    capacity.
     """
     q, k, v, seq_lens = inputs["q"], inputs["k"], inputs["v"], inputs["seq_lens"]
     B, Hkv, lmax, d = k.shape
@@ -258,4 +272,9 @@ def append_token(inputs: dict, gen: torch.Generator) -> None:
     k[bidx, :, pos] = new_k
     v[bidx, :, pos] = new_v
     q.copy_(_normal_bf16(tuple(q.shape), gen, dev))
+    k_nope, q_nope = inputs.get("k_nope", k), inputs.get("q_nope", q)
+    if k_nope is not k:
+        k_nope[bidx, :, pos] = _normal_bf16((B, Hkv, d), gen, dev)
+    if q_nope is not q:
+        q_nope.copy_(_normal_bf16(tuple(q_nope.shape), gen, dev))
     seq_lens.add_(1)
