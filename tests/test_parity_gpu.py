@@ -866,8 +866,9 @@ def test_fused_step_equals_staged(S, name, overrides):
 
 
 SK_CASES = [
-    # lengths from 40 to 20000 tokens, threshold: 2 to ~150 blocks per pair
-    ("threshold_b128", dict(batch=5, max_seq_len=20000, seq_len_range=(40, 20000)), None),
+    # lengths from 40 to 20000 tokens, threshold: 1 to ~150 blocks per pair
+    ("threshold_b128", dict(batch=5, max_seq_len=20000, seq_len_range=(40, 20000)),
+     [40, 700, 5000, 12000, 20000]),
     # one long sequence among short ones: its pairs span many workgroups,
     # more parts than the merge holds in registers
     ("qwen3_14b_b16", dict(batch=4, mode="topp", tau=0.97), [32768, 700, 64, 1]),
