@@ -382,7 +382,10 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   seer::GateArgs ga{};
   ga.q_nope = q_nope;
   ga.w_q = w_q;
-  ga.q_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec_bytes);
+  // the gate's scratch first (a fixed place whatever the split count), then
+  // the decode workspace
+  char* ws = static_cast<char*>(workspace);
+  ga.q_gate = reinterpret_cast<float*>(ws);
   ga.theta = rope_theta;
   ga.k_nope = k_nope;
   ga.w_k = w_k;
@@ -400,7 +403,7 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   rc = seer::launch_gate(*dims, ga, stream);
   if (rc != SEER_OK) return rc;
   return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,
-                       scale, s, workspace, dec_bytes, out, lse, stream,
+                       scale, s, ws + seer::step_gate_bytes(dims), dec_bytes, out, lse, stream,
                        inline_new > 0 ? kcomp_lens : nullptr, inline_new, nullptr, stream_k);
 }
 

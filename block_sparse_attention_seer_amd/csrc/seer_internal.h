@@ -31,7 +31,7 @@ int check_ptr(const void* p, size_t align, const char* name, std::string* why);
 
 int64_t nb_max(const seer_dims* d);  // ceil(Lmax / b)
 size_t gate_workspace_bytes(const seer_dims* d);
-// Gate-query scratch of the fused step, rounded up to 256 bytes.
+// The gate queries inside the fused step's workspace, rounded up to 256 bytes.
 size_t step_gate_bytes(const seer_dims* d);
 // Workspace of the decode kernel for `pairs` (b, h) pairs, `num_split`
 // splits and group size g: the per-split lse and outputs.

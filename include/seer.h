@@ -25,8 +25,9 @@
  *   - The caller owns every buffer.  The library allocates nothing and keeps
  *     no pointer after a call returns.  Outputs are fully overwritten
  *     (including padding), so callers never pre-initialise them; the only
- *     exception is the decode workspace, which must be zero-filled once
- *     before its first use (see seer_decode_workspace_bytes).
+ *     exceptions are the decode and fused-step workspaces, which hold
+ *     counters and must be zero-filled once before their first use (every
+ *     call leaves the counters zero again).
  *   - Host-detectable errors return before anything is launched; nothing is
  *     written.  A kernel launch failure returns SEER_ERR_HIP.  Device-side
  *     data problems cannot be reported synchronously: out-of-range lengths
@@ -329,8 +330,10 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
  *                    writing them.
  *   scale, num_split as seer_sparse_decode.
  *   workspace        >= seer_decode_step_workspace_bytes(dims, max_selected,
- *                    num_split) bytes, 256-byte aligned: the decode workspace
- *                    (zero before first use) followed by the gate queries.
+ *                    num_split) bytes, 256-byte aligned: the gate workspace
+ *                    (rounded up to 256 bytes), then the decode workspace;
+ *                    both hold counters, so zero-fill the whole workspace
+ *                    before its first use (every call leaves them zero).
  *                    With num_split = 0 the size includes the stream-K
  *                    decode's per-workgroup partials; a workspace sized for
  *                    the split decode alone is still accepted (no stream-K).

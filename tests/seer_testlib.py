@@ -80,6 +80,15 @@ def assert_gt_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> None:
                            f"{float(np.nanmax(err - bound)):.3e} over the bound")
 
 
+def step_decode_counters(st) -> torch.Tensor:
+    """The per-(b, h) split counters of a DecodeStep's fused-step workspace
+    (int32 view): they follow the gate workspace, rounded up to 256 bytes."""
+    import block_sparse_attention_seer_amd as S
+    d = st.dims
+    off = -(-S.seer_gate_workspace_bytes(d) // 256) * 256 // 4
+    return st.step_ws.view(torch.int32)[off:off + d.batch * d.num_kv_heads]
+
+
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
     """Spacing of bf16 values at |x| (2^(e-8) for x = m 2^e, 0.5 <= m < 1)."""
     _, e = np.frexp(np.where(x == 0, 1.0, x))

@@ -17,7 +17,8 @@ import torch
 
 import oracle as O
 from seer_testlib import (assert_lse_close, assert_out_close, bf16_ulp, check_topk_set,
-                          check_topp_set, f64, host_inputs, oracle_chain, threshold_value)
+                          check_topp_set, f64, host_inputs, oracle_chain, step_decode_counters,
+                          threshold_value)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -565,6 +566,9 @@ def test_gate_matches_oracle(S, B, Hq, Hkv, d, dg, bs, lens):
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
     st.build_cache(k.to(DEV), wk.to(DEV), seq)
     st.logits.fill_(float("nan"))
+    # the gate queries are exchanged through the workspace: stale values
+    # there (NaN) must never be read
+    st.gate_ws[: B * Hkv * dg].fill_(float("nan"))
     S.seer_gate_scores(dims, qn.to(DEV), wq.to(DEV), st.kcomp, st.kcomp_lens, seq, st.gate_ws,
                        st.logits, 10000.0)
     torch.cuda.synchronize()
@@ -838,6 +842,9 @@ def test_fused_step_equals_staged(S, name, overrides):
     _clone_state(a, b)
     _clone_state(a, c)
     c.logits.fill_(123.0)
+    # stale gate queries in the fused workspace (it starts with them) are never read
+    for x in (b, c):
+        x.step_ws[: w.batch * w.num_kv_heads * w.d_gate].fill_(float("nan"))
     args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
     a.step(*args)
     b.fused_step(*args)
@@ -857,7 +864,7 @@ def test_fused_step_equals_staged(S, name, overrides):
     # the fused workspace's split counters (its first B*Hkv ints, present
     # when the decode splits) are left at zero
     if b.num_split > 1 or stream_k:
-        assert int(b.step_ws[: w.batch * w.num_kv_heads].view(torch.int32).abs().sum()) == 0
+        assert int(step_decode_counters(b).abs().sum()) == 0
     # pairs against the oracle as well: all of them for stream-K
     pairs = ([(bb, hh) for bb in range(w.batch) for hh in range(w.num_kv_heads)] if stream_k
              else [(w.batch - 1, w.num_kv_heads - 1)])
@@ -912,7 +919,7 @@ def test_fused_step_stream_k_matches_oracle(S, name, overrides, lens):
     assert torch.equal(first[0].view(torch.int16), st.out.view(torch.int16))
     assert torch.equal(first[1].view(torch.int32), st.lse.view(torch.int32))
     pairs = w.batch * w.num_kv_heads
-    assert int(st.step_ws[:pairs].view(torch.int32).abs().sum()) == 0
+    assert int(step_decode_counters(st).abs().sum()) == 0
     nsel = st.num_selected.cpu()
     assert int(nsel.max()) > 4 * max(int(nsel.min()), 1)  # the selections are uneven
     g = w.group
@@ -1145,7 +1152,7 @@ def test_bound_step_equals_staged(S, num_split, mode):
     assert completed > 0
     # the split counters at the start of the workspace are back at zero
     pairs = w.batch * w.num_kv_heads
-    assert int(fused.step_ws.view(torch.int32)[:pairs].abs().sum()) == 0
+    assert int(step_decode_counters(fused).abs().sum()) == 0
     _check_pair(w, inp, fused, 1, 3, "bound step vs oracle")
 
 
