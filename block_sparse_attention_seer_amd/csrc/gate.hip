@@ -32,11 +32,6 @@ namespace seer {
 
 namespace {
 
-RopeFreqs make_freqs(int dg, double theta) {
-  RopeFreqs f{};
-  for (int i = 0; i < dg / 2; ++i) f.w[i] = std::pow(theta, -2.0 * i / dg);
-  return f;
-}
 
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
@@ -59,7 +54,7 @@ struct PrepParams {
   const int32_t* seq_lens;
   int64_t sb, sh, st;
   int Hkv, BS, Lmax, NBmax;
-  RopeFreqs freqs;
+  double log2_theta;  // RoPE base, as log2
 };
 
 template <int D, int DG>
@@ -76,7 +71,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
   cl = min(max(cl, 0), p.NBmax);
   const int j = cl + z;
   if (j >= L / p.BS) return;  // uniform over the workgroup
-  const double wf = p.freqs.w[threadIdx.x % (DG / 2)];
+  const double wf = rope_freq(threadIdx.x % (DG / 2), DG, p.log2_theta);
   const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j) * p.BS * p.st;
   uint16_t* dst = p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j) * DG;
   compress_block<D, DG>(cm, keys, p.st, p.BS, p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf, j,
@@ -104,7 +99,7 @@ __global__ __launch_bounds__(256) void prep_bulk_kernel(PrepParams p) {
   const int j0 = cl + z0;
   const int nblk = min(kBulkBlocks, min(L / p.BS, cl + p.max_new) - j0);
   if (nblk <= 0) return;  // uniform over the workgroup
-  const double wf = p.freqs.w[threadIdx.x % (DG / 2)];
+  const double wf = rope_freq(threadIdx.x % (DG / 2), DG, p.log2_theta);
   const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(j0) * p.BS * p.st;
   uint16_t* dst = p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + j0) * DG;
   compress_blocks<D, DG, kBulkBlocks>(cm, keys, p.st, p.BS,
@@ -147,14 +142,17 @@ struct GateParams {
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
   float* logits_out;   // [B, H_kv, NBmax] or null
-  int32_t* block_idx;  // select when non-null
+  int32_t* scored_out; // [B, H_kv]: the number of scored blocks, or null
+  int32_t* block_idx;  // select when non-null (one row part only)
   int32_t* num_selected;
+  int pairs;           // B * H_kv; workgroup = part * pairs + pair
+  int rows_per_part;   // logit rows of one workgroup (a multiple of 64)
   int Hq, Hkv, G, BS, Lmax, NBmax;
   int mode, topk, max_sel;
   float log_tau;
   uint32_t mass_target;  // top-p: ceil(p * 2^30)
   float inv_sqrt_dg;
-  RopeFreqs freqs;
+  double log2_theta;  // RoPE base, as log2
 };
 
 // Chunk group c0 .. c0+kQueryChunks-1 (128 dims each) of this lane's W_q
@@ -181,19 +179,23 @@ __device__ __forceinline__ void load_query_group(uint4 (&wb)[TQ][kQueryChunks],
 }
 
 // This lane's pieces of the cache rows of one pass that are already cached
-// (j < nc0); the rest are zero.
+// and in this workgroup's rows (j < lim); the rest are zero.
 template <int TPW, int RPT, int P, int DG>
-__device__ __forceinline__ void load_rows(uint4 (&kv)[TPW], const uint16_t* kc, int row0, int nc0,
+__device__ __forceinline__ void load_rows(uint4 (&kv)[TPW], const uint16_t* kc, int row0, int lim,
                                           int n) {
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int j = row0 + t * RPT + n / P;
-    kv[t] = (j < nc0) ? ld16(kc + static_cast<int64_t>(row0 + t * RPT) * DG)
+    kv[t] = (j < lim) ? ld16(kc + static_cast<int64_t>(row0 + t * RPT) * DG)
                       : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
-// One 512-thread workgroup per (sequence, KV head).
+// One 512-thread workgroup per (sequence, KV head) and part of its cache
+// rows: with more than one part, each workgroup of a pair computes the gate
+// query (so no workgroup waits for another) and the logits of its own rows
+// [part * rows_per_part, +rows_per_part); the selection then runs in the
+// decode launch.  A logit's arithmetic does not depend on the part count.
 //
 // Both contractions use the same MFMA layout.  A 16-column tile covers
 // 16/P rows of a matrix, each split into P parts of 32 dims: column n is
@@ -225,7 +227,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   __shared__ uint16_t s_new[kMaxInlineNew][DG];  // this launch's new cache entries
   __shared__ CompressSmem<D, DG, kMaxInlineNew> s_cm;
 
-  const int pair = blockIdx.x;
+  const int part = blockIdx.x / p.pairs;
+  const int pair = blockIdx.x - part * p.pairs;
+  const int r0 = part * p.rows_per_part;          // this workgroup's logit rows
+  const int r1 = min(p.NBmax, r0 + p.rows_per_part);
   const int b = pair / p.Hkv;
   const int h = pair - b * p.Hkv;
   const int tid = threadIdx.x;
@@ -239,17 +244,20 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   int nc0 = p.kcomp_lens[b];
   nc0 = min(min(max(nc0, 0), p.NBmax), L / p.BS);  // cached blocks
   const int nc = min(L / p.BS, nc0 + p.max_new);   // scored: with this launch's entries
-  const int nnew = nc - nc0;
+  // this launch's new entries that fall in this workgroup's rows
+  const int e0 = max(nc0, r0);
+  const int nnew = max(0, min(nc, r1) - e0);
   select_smem_init(s_sel);
-  const double wf = p.freqs.w[tid % (DG / 2)];
+  const double wf = rope_freq(tid % (DG / 2), DG, p.log2_theta);
+  if (part == 0 && p.scored_out != nullptr && tid == 0) p.scored_out[pair] = nc;
 
   // ---- new cache entries (blocks completed since the last update), in one
   // pass before anything else is in flight (they are rare: one step in b)
   if (nnew > 0) {
-    const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(nc0) * p.BS * p.st;
+    const uint16_t* keys = p.k_nope + b * p.sb + h * p.sh + static_cast<int64_t>(e0) * p.BS * p.st;
     compress_blocks<D, DG, kMaxInlineNew>(s_cm, keys, p.st, p.BS,
-                                          p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf, nc0,
-                                          nnew, p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + nc0) * DG,
+                                          p.w_k + static_cast<int64_t>(h) * DG * 3 * D, wf, e0,
+                                          nnew, p.kcomp + (static_cast<int64_t>(pair) * p.NBmax + e0) * DG,
                                           &s_new[0][0]);
   }
 
@@ -269,9 +277,11 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   load_query_group<TQ>(wb, xa, wq, xq, 0, nch, K, n, g, wr);
 
   const uint16_t* kc = p.kcomp + static_cast<int64_t>(pair) * p.NBmax * DG + 32 * n + 8 * g;
-  const int passes = max(1, (nc + kGateRows - 1) / kGateRows);
-  uint4 kv[TPW];  // rows already cached; this launch's entries come from LDS
-  load_rows<TPW, RPT, P, DG>(kv, kc, w * RPW, nc0, n);
+  const int rows_scored = max(0, min(nc, r1) - r0);  // rows r0 .. of this workgroup
+  const int passes = (rows_scored + kGateRows - 1) / kGateRows;
+  const int lim = min(nc0, r1);  // rows read from the cache (the rest: this launch's entries)
+  uint4 kv[TPW];
+  if (passes > 0) load_rows<TPW, RPT, P, DG>(kv, kc, r0 + w * RPW, lim, n);
 
   // ---- gate query: y = W_q[h] x, then RoPE at position L-1
   {
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
     rope_pair(static_cast<double>(L - 1), wf, ylo, yhi, &olo, &ohi);
     s_qg[tid] = olo;
     s_qg[tid + DG / 2] = ohi;
-    if (p.q_gate_out != nullptr) {
+    if (p.q_gate_out != nullptr && part == 0) {
       p.q_gate_out[static_cast<int64_t>(pair) * DG + tid] = olo;
       p.q_gate_out[static_cast<int64_t>(pair) * DG + tid + DG / 2] = ohi;
     }
@@ -323,14 +333,14 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   const bool diag = (g < P) && (g == n % P);
   float* lo = p.logits_out ? p.logits_out + static_cast<int64_t>(pair) * p.NBmax : nullptr;
   for (int pass = 0; pass < passes; ++pass) {
-    const int row0 = pass * kGateRows + w * RPW;  // first row of this wave
-    if (pass > 0) load_rows<TPW, RPT, P, DG>(kv, kc, row0, nc0, n);
+    const int row0 = r0 + pass * kGateRows + w * RPW;  // first row of this wave
+    if (pass > 0) load_rows<TPW, RPT, P, DG>(kv, kc, row0, lim, n);
     if (nnew > 0) {  // this launch's entries, from LDS
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int j = row0 + t * RPT + n / P;
-        if (j >= nc0 && j < nc)
-          kv[t] = *reinterpret_cast<const uint4*>(&s_new[j - nc0][32 * (n % P) + 8 * g]);
+        if (j >= e0 && j < e0 + nnew)
+          kv[t] = *reinterpret_cast<const uint4*>(&s_new[j - e0][32 * (n % P) + 8 * g]);
       }
     }
 #pragma unroll
@@ -346,13 +356,13 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
 #pragma unroll
       for (int q = 1; q < P; ++q) z += pp[q];
       z *= p.inv_sqrt_dg;
-      if (j < nc) s_keys[j] = __float_as_uint(z);
-      if (lo != nullptr && j < p.NBmax) lo[j] = (j < nc) ? z : -INFINITY;
+      if (j < min(nc, r1)) s_keys[j] = __float_as_uint(z);
+      if (lo != nullptr && j < r1) lo[j] = (j < nc) ? z : -INFINITY;
     }
     wave_lds_order();  // the next pass rewrites this wave's part sums
   }
-  if (lo != nullptr)  // rows past the passes walked above
-    for (int j = passes * kGateRows + tid; j < p.NBmax; j += kGateThreads) lo[j] = -INFINITY;
+  if (lo != nullptr)  // this workgroup's rows past the passes walked above
+    for (int j = r0 + passes * kGateRows + tid; j < r1; j += kGateThreads) lo[j] = -INFINITY;
   if (p.block_idx == nullptr) return;
   __syncthreads();
   select_blocks_wg<kGateThreads>(s_keys, s_sel, nc, (L + p.BS - 1) / p.BS, p.mode, p.topk,
@@ -368,8 +378,6 @@ void launch_gate_t(const GateParams& p, int grid, size_t lds, hipStream_t s) {
 
 }  // namespace
 
-float log_threshold(float tau);
-uint32_t topp_mass_target(float p);
 
 int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   PrepParams p{};
@@ -386,7 +394,7 @@ int launch_prep(const seer_dims& d, const PrepArgs& a, void* stream) {
   p.BS = d.block_size;
   p.Lmax = d.max_seq_len;
   p.NBmax = static_cast<int>(nb_max(&d));
-  p.freqs = make_freqs(d.d_gate, a.theta);
+  p.log2_theta = std::log2(a.theta);
   const bool bulk = a.max_new_blocks >= kBulkBlocks;
   const int64_t per_pair = bulk ? (a.max_new_blocks + kBulkBlocks - 1) / kBulkBlocks
                                 : a.max_new_blocks;
@@ -435,8 +443,11 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   p.kcomp_lens = a.kcomp_lens;
   p.seq_lens = a.seq_lens;
   p.logits_out = a.logits_out;
+  p.scored_out = a.scored_out;
   p.block_idx = a.block_idx;
   p.num_selected = a.num_selected;
+  const int64_t pairs = static_cast<int64_t>(d.batch) * d.num_kv_heads;
+  p.pairs = static_cast<int>(pairs);
   p.Hq = d.num_q_heads;
   p.Hkv = d.num_kv_heads;
   p.G = d.num_q_heads / d.num_kv_heads;
@@ -449,8 +460,15 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   p.log_tau = log_threshold(a.tau);
   p.mass_target = topp_mass_target(a.tau);
   p.inv_sqrt_dg = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d_gate)));
-  p.freqs = make_freqs(d.d_gate, a.theta);
-  const int64_t grid = static_cast<int64_t>(d.batch) * d.num_kv_heads;
+  p.log2_theta = std::log2(a.theta);
+  // row parts: every one non-empty (rows_per_part a multiple of 64); the
+  // selection needs the whole row in one workgroup
+  const int nbm = p.NBmax;
+  int parts = (a.block_idx != nullptr) ? 1 : std::max(1, std::min(a.row_parts, (nbm + 63) / 64));
+  int rpp = ((nbm + parts - 1) / parts + 63) / 64 * 64;
+  parts = (nbm + rpp - 1) / rpp;
+  p.rows_per_part = rpp;
+  const int64_t grid = pairs * parts;
   if (grid > 0x7fffffff) {
     set_error("gate grid too large");
     return SEER_ERR_UNSUPPORTED;

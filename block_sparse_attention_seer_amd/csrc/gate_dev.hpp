@@ -16,11 +16,13 @@
 
 namespace seer {
 
-// RoPE frequencies theta^(-2i/d_gate), i < d_gate/2, formed on the host in
-// float64 and passed by value.
-struct RopeFreqs {
-  double w[64];
-};
+// RoPE frequency theta^(-2i/D) of pair i, formed in float64 from log2(theta)
+// (the exponent 2i/D is exact for the power-of-two D here).  Computed where
+// it is used rather than passed as a table: a table in the kernel arguments
+// is loaded by every wave into scalar registers.
+__device__ __forceinline__ double rope_freq(int i, int D, double log2_theta) {
+  return exp2((-2.0 * static_cast<double>(i) / static_cast<double>(D)) * log2_theta);
+}
 
 // Rotate-half RoPE of the pair (lo, hi) = (x_i, x_{i+D/2}) at angle pos*w.
 // The angle (up to ~1e5 rad) is formed and reduced to [-pi, pi] in float64

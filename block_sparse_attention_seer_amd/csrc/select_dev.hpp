@@ -40,14 +40,18 @@
 namespace seer {
 
 constexpr int kSelMaxWaves = 16;
+constexpr int kSelCand = 32;  // top-k fast path: boundary-bucket keys ranked directly
 
-struct SelectSmem {
-  int hist[256];
+struct alignas(16) SelectSmem {
+  int hist[256];  // 16-byte aligned: the top-k fast path reads it four at a time
   int hmass[256];  // top-p: per-bucket mass in units of 2^-30 of the total
   float fred[2][kSelMaxWaves];
   uint32_t ured[2][kSelMaxWaves];
   int scan[2][kSelMaxWaves];
   int pick[4];
+  uint32_t cand_key[kSelCand];  // top-k fast path: the boundary bucket's keys
+  int cand_idx[kSelCand];
+  int ncand;
 };
 
 // Clears the histograms; call with every thread, then a barrier, before the
@@ -57,6 +61,7 @@ __device__ __forceinline__ void select_smem_init(SelectSmem& sm) {
     sm.hist[threadIdx.x] = 0;
     sm.hmass[threadIdx.x] = 0;
   }
+  if (threadIdx.x == 0) sm.ncand = 0;
 }
 
 // Top-p mass unit: 2^30 units make the whole softmax.
@@ -524,6 +529,143 @@ __device__ __forceinline__ void select_blocks_impl(const uint32_t* keys, SelectS
   if (tid == 0) *count_out = written;
 }
 
+// Top-k when every thread holds at most one key (nc <= NT) and 0 < k < nc,
+// in three or four workgroup barriers (the general narrowing above takes
+// seven): the value histogram is scanned by every wave itself, and the
+// bucket holding the k-th largest key is resolved by ranking its few keys
+// against each other instead of by further histogram passes.  It selects
+// the same set as the narrowing (the k largest; equal logits: lower index
+// first).  Returns false, having written nothing and with the histograms
+// zero, when it does not apply (the caller then runs the narrowing).
+//   1. wave min / max of the logits to LDS; barrier;
+//   2. every thread: the workgroup min / max, then its key's bucket among
+//      256 linear buckets on [min, max] into the histogram; barrier;
+//   3. every wave: the histogram scan -> bucket b, the count above it, its
+//      count m (identical in every wave);
+//   4. if m keys exceed what is still needed: b's keys append (key, index)
+//      to a list; barrier; each counts the list entries ahead of it
+//      (m > kSelCand: not applicable);
+//   5. the ascending output: per-wave ballot counts; barrier; prefix; write.
+template <int NT>
+__device__ __forceinline__ bool select_topk_one_key(const uint32_t* keys, SelectSmem& sm, int nc,
+                                                    int total_blocks, int k, int max_sel,
+                                                    int32_t* out, int32_t* count_out) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const bool have = tid < nc;
+  const float z = have ? __uint_as_float(keys[tid]) : 0.f;
+  // 1.
+  {
+    const float mn = wave_min(have ? z : INFINITY);
+    const float mx = wave_max(have ? z : -INFINITY);
+    if (lane == 0) {
+      sm.fred[0][w] = mn;
+      sm.fred[1][w] = mx;
+    }
+  }
+  __syncthreads();
+  // 2.
+  float zmn = sm.fred[0][0], zmx = sm.fred[1][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    zmn = fminf(zmn, sm.fred[0][i]);
+    zmx = fmaxf(zmx, sm.fred[1][i]);
+  }
+  const float scale = 256.f / (zmx - zmn);
+  if (!(zmx > zmn && scale > 0.f && scale < INFINITY)) {  // uniform
+    __syncthreads();  // every wave has read fred before the narrowing rewrites it
+    return false;
+  }
+  const int bkt = (z == z) ? min(255, static_cast<int>((z - zmn) * scale)) : 0;
+  if (have) atomicAdd(&sm.hist[bkt], 1);
+  __syncthreads();
+  // 3. every wave: lane l holds buckets 4l .. 4l+3
+  int b_star, above, m;
+  {
+    const int4 h4 = *reinterpret_cast<const int4*>(&sm.hist[4 * lane]);
+    const int hb[4] = {h4.x, h4.y, h4.z, h4.w};
+    const int mine = (hb[0] + hb[1]) + (hb[2] + hb[3]);
+    const int incl = wave_inclusive_scan(mine);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int suf = total - incl + mine;  // keys in buckets >= 4 lane
+    int cnt = suf - mine;                 // keys in buckets >= 4 lane + 4
+    int pick = -1, pa = 0, pm = 0;
+    if (cnt < k && k <= suf) {
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (pick < 0 && cnt + hb[i] >= k) {
+          pick = 4 * lane + i;
+          pa = cnt;
+          pm = hb[i];
+        }
+        cnt += hb[i];
+      }
+    }
+    const unsigned long long who = __ballot(pick >= 0);
+    const int src = __builtin_ffsll(static_cast<long long>(who)) - 1;  // exactly one lane
+    b_star = __builtin_amdgcn_readlane(pick, src);
+    above = __builtin_amdgcn_readlane(pa, src);
+    m = __builtin_amdgcn_readlane(pm, src);
+  }
+  const int need = k - above;  // 1 <= need <= m
+  if (m > need && m > kSelCand) {  // uniform: leave it to the narrowing
+    __syncthreads();               // every wave has read the histogram
+    if (tid < 256) sm.hist[tid] = 0;
+    __syncthreads();
+    return false;
+  }
+  bool taken = have && bkt > b_star;
+  if (m == need) {
+    taken = taken || (have && bkt == b_star);
+  } else {
+    // 4. rank the boundary bucket's keys: (key descending, index ascending)
+    const uint32_t key = float_key(z);
+    if (have && bkt == b_star) {
+      const int slot = atomicAdd(&sm.ncand, 1);
+      sm.cand_key[slot] = key;
+      sm.cand_idx[slot] = tid;
+    }
+    __syncthreads();
+    if (have && bkt == b_star) {
+      int ahead = 0;
+      for (int c = 0; c < m; ++c) {
+        const uint32_t kc = sm.cand_key[c];
+        ahead += (kc > key) || (kc == key && sm.cand_idx[c] < tid);
+      }
+      taken = ahead < need;
+    }
+  }
+  // 5. positions in index order (thread order)
+  const unsigned long long bal = __ballot(taken);
+  const int before_in_wave = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) sm.scan[1][w] = __builtin_popcountll(bal);
+  __syncthreads();
+  if (tid < 256) sm.hist[tid] = 0;  // left zero, as the narrowing leaves them
+  if (tid == 0) sm.ncand = 0;
+  int before = 0, scored_total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int c = sm.scan[1][i];
+    before += (i < w) ? c : 0;
+    scored_total += c;
+  }
+  // forced blocks first when the row is short (the caller's k fits them)
+  const int forced = max(0, total_blocks - nc);
+  const int kept_forced = min(forced, max_sel);
+  const int room = max_sel - kept_forced;
+  const int pos = before + before_in_wave;
+  if (taken && pos < room) out[pos] = tid;
+  const int scored_written = min(scored_total, room);
+  const int f0 = total_blocks - kept_forced;
+  for (int f = tid; f < kept_forced; f += NT) out[scored_written + f] = f0 + f;
+  const int written = scored_written + kept_forced;
+  for (int i = written + tid; i < max_sel; i += NT) out[i] = -1;
+  if (tid == 0) *count_out = written;
+  return true;
+}
+
 // Called by all NT threads once keys[0..nc) (LDS, the logits as float bits)
 // are visible to every one of them.  The histograms (select_smem_init) must
 // be zero on entry and are left zero.  mass_target = ceil(p * 2^30) for
@@ -536,6 +678,13 @@ __device__ __forceinline__ void select_blocks_wg(const uint32_t* keys, SelectSme
                                                  float log_tau, uint32_t mass_target,
                                                  int max_sel, int32_t* out, int32_t* count_out) {
   const int vpt = (nc + NT - 1) / NT;
+  if (mode == SEER_SELECT_TOPK && vpt <= 1) {
+    const int forced = max(0, total_blocks - nc);
+    const int k = min(min(topk, nc), max_sel - min(forced, max_sel));
+    if (k > 0 && k < nc &&
+        select_topk_one_key<NT>(keys, sm, nc, total_blocks, k, max_sel, out, count_out))
+      return;
+  }
   if (vpt <= 1)
     select_blocks_impl<NT, 1>(keys, sm, nc, total_blocks, mode, topk, log_tau, mass_target,
                               max_sel, out, count_out);
