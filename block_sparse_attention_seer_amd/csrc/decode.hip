@@ -44,13 +44,7 @@
 //   * selections of very different sizes (threshold, top-p) can instead be
 //     divided stream-K: each workgroup takes an equal share of all pairs'
 //     chunks, decodes the pairs in it one after another, and a pair cut
-//     between shares merges through the same counter protocol;
-//   * in the fused step the selection itself can run here (SEL): every
-//     workgroup of a pair reads the pair's block logits, selects with the
-//     routine of the select kernel into an LDS index row, and the pair's
-//     first split also writes that row out.  The gate launch before it then
-//     only scores, spread over more workgroups.
-#include "select_dev.hpp"
+//     between shares merges through the same counter protocol.
 #include "seer_device.hpp"
 #include "seer_internal.h"
 
@@ -91,16 +85,6 @@ struct DecodeParams {
   const int32_t* block_table;
   int table_stride, num_pages;
   int64_t page_stride, page_head_stride;
-  // selection in this launch (SEL): the logits [pairs, NBmax] and scored
-  // counts [pairs] the gate launch left; block_idx / num_selected are then
-  // outputs, written by each pair's first split
-  const float* sel_logits;
-  const int32_t* sel_scored;
-  int32_t* sel_block_idx;
-  int32_t* sel_num_selected;
-  int sel_mode, sel_topk;
-  float sel_log_tau;
-  uint32_t sel_mass;
 };
 
 // bf16 j (0..3) of a's four values in the low half, of b's in the high half.
@@ -121,8 +105,6 @@ struct Part {
   int c_begin, c_end;    // stream-K
   int nparts;
   int64_t my_slot, slot0, slot1, slot_step;
-  const int* row;        // the index row in LDS (selection in this launch), or null
-  int row_count;
 };
 
 template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK>
@@ -147,10 +129,9 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
 
   const int32_t* idx = DENSE ? nullptr : p.block_idx + static_cast<int64_t>(pair) * p.max_sel;
   // The first kIdxLds entries of the index row go to LDS, requested at once
-  // with the selection count instead of after it (unless the whole row is
-  // already in LDS: the selection ran in this launch).
+  // with the selection count instead of after it.
   __shared__ int s_idx[kIdxLds];
-  if (!DENSE && pt.row == nullptr) {
+  if (!DENSE) {
     // a stream-K part stages only the entries of its own chunks
     const int i_end = min(p.max_sel, kIdxLds);
     const int i_lo = SK ? min(pt.c_begin / CPB, i_end) : 0;
@@ -169,8 +150,6 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
   int nslots;
   if (DENSE) {
     nslots = nblk;
-  } else if (pt.row != nullptr) {
-    nslots = pt.row_count;
   } else {
     nslots = p.num_selected[pair];
     nslots = min(max(nslots, 0), p.max_sel);
@@ -209,9 +188,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
 
   for (int c = c_begin + w; c < c_end; c += NW) {
     const int slot = c / CPB;
-    const int blk = DENSE ? slot
-                          : (pt.row != nullptr ? pt.row[slot]
-                                               : (slot < kIdxLds ? s_idx[slot] : idx[slot]));
+    const int blk = DENSE ? slot : (slot < kIdxLds ? s_idx[slot] : idx[slot]);
     const int base = blk * BS + (c - slot * CPB) * (16 * TPC);
     if (blk < 0 || blk >= nblk || base >= L) continue;  // invalid entry: skipped
     // row 0 of the chunk's block in the cache
@@ -555,14 +532,9 @@ __device__ __forceinline__ int sk_group_of(int x, int T, int N) {
 // one after another.  A pair inside one share writes its output directly; a
 // pair cut between shares is merged by the last of its parts to finish, as
 // fixed splits are.  Nothing waits on another workgroup in either scheme.
-template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK, bool SEL>
+template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK>
 __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
-  // [NW][G][D] floats for the wave merge.  With SEL the selection's keys
-  // (NBmax words) share its start (they are dead once the row is built), and
-  // the index row (max_sel words) follows both: waves read the row until
-  // their loop ends, while a wave done with its loop already writes its
-  // merge data.
-  extern __shared__ float sm_o[];
+  extern __shared__ float sm_o[];  // [NW][G][D]
   const int tid = threadIdx.x;
 
   // Fused step: the cache entries appended by this step's gate launch are
@@ -583,37 +555,6 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
     pt.my_slot = pt.slot0 + pt.split;
     pt.slot1 = pt.slot0 + 1;
     pt.slot_step = 1;
-    if constexpr (SEL) {
-      static_assert(!DENSE && !PAGED, "selection in the launch: contiguous sparse decode");
-      // [CP Knowl 5]: binarise this pair's block scores (the gate launch's
-      // logits) into its active blocks, exactly as the select kernel does
-      __shared__ SelectSmem s_sel;
-      __shared__ int s_count;
-      // the whole logit row is requested together with the length and the
-      // scored count (the gate launch left -inf past the count), so the
-      // keys arrive in one round trip
-      const int b = pt.pair / p.Hkv;
-      uint32_t* keys = reinterpret_cast<uint32_t*>(sm_o);
-      int* row = reinterpret_cast<int*>(sm_o) + max(NW * p.G * D, p.NBmax);
-      const float* z = p.sel_logits + static_cast<int64_t>(pt.pair) * p.NBmax;
-      for (int j = tid; j < p.NBmax; j += NW * 64) keys[j] = __float_as_uint(z[j]);
-      int L = p.seq_lens[b];
-      L = min(max(L, 0), p.Lmax);
-      int nc = p.sel_scored[pt.pair];
-      nc = min(max(nc, 0), min(p.NBmax, L / p.BS));
-      select_smem_init(s_sel);
-      __syncthreads();
-      select_blocks_wg<NW * 64>(keys, s_sel, nc, (L + p.BS - 1) / p.BS, p.sel_mode, p.sel_topk,
-                                p.sel_log_tau, p.sel_mass, p.max_sel, row, &s_count);
-      __syncthreads();
-      pt.row = row;
-      pt.row_count = min(max(s_count, 0), p.max_sel);
-      if (pt.split == 0) {  // the step's outputs
-        int32_t* out = p.sel_block_idx + static_cast<int64_t>(pt.pair) * p.max_sel;
-        for (int i = tid; i < p.max_sel; i += NW * 64) out[i] = row[i];
-        if (tid == 0) p.sel_num_selected[pt.pair] = pt.row_count;
-      }
-    }
     decode_part<D, BS, DENSE, NW, PAGED, false>(p, pt, sm_o);
   } else {
     static_assert(!DENSE, "stream-K division is for selections");
@@ -707,24 +648,11 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK = false, bool SEL = false>
+template <int D, int BS, bool DENSE, int NW, bool PAGED, bool SK = false>
 void launch_one(const DecodeParams& p, int grid, hipStream_t stream) {
-  size_t lds = static_cast<size_t>(NW) * p.G * D * sizeof(float);
-  if (SEL)
-    lds = (std::max(lds / sizeof(float), static_cast<size_t>(p.NBmax)) + p.max_sel) * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW, PAGED, SK, SEL>), dim3(grid), dim3(NW * 64),
-                     lds, stream, p);
-}
-
-// selection in the launch: selections over a contiguous cache
-template <int NW>
-void launch_variant_sel(int key, const DecodeParams& p, int grid, hipStream_t s) {
-  switch (key) {
-    case 0: launch_one<64, 64, false, NW, false, false, true>(p, grid, s); break;
-    case 2: launch_one<64, 128, false, NW, false, false, true>(p, grid, s); break;
-    case 4: launch_one<128, 64, false, NW, false, false, true>(p, grid, s); break;
-    default: launch_one<128, 128, false, NW, false, false, true>(p, grid, s); break;
-  }
+  const size_t lds = static_cast<size_t>(NW) * p.G * D * sizeof(float);
+  hipLaunchKernelGGL((decode_kernel<D, BS, DENSE, NW, PAGED, SK>), dim3(grid), dim3(NW * 64), lds,
+                     stream, p);
 }
 
 // stream-K: selections over a contiguous cache
@@ -787,21 +715,12 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   p.num_pages = a.num_pages;
   p.page_stride = a.page_stride;
   p.page_head_stride = a.page_head_stride;
-  const bool sel = a.sel_logits != nullptr;
-  p.sel_logits = a.sel_logits;
-  p.sel_scored = a.sel_scored;
-  p.sel_block_idx = a.sel_block_idx;
-  p.sel_num_selected = a.sel_num_selected;
-  p.sel_mode = a.sel_mode;
-  p.sel_topk = a.sel_topk;
-  p.sel_log_tau = log_threshold(a.sel_tau);
-  p.sel_mass = topp_mass_target(a.sel_tau);
-  const bool dense = (a.block_idx == nullptr) && !sel;
+  const bool dense = (a.block_idx == nullptr);
   const bool paged = a.block_table != nullptr;
   const int nw = decode_waves_per_group(G, d.head_dim);
   // stream-K where it applies: a selection over a contiguous cache, with the
   // pairs' prefix and the wave merge both in LDS
-  const bool sk = !sel && a.stream_k && !dense && !paged && pairs <= kSkMaxPairs &&
+  const bool sk = a.stream_k && !dense && !paged && pairs <= kSkMaxPairs &&
                   static_cast<int64_t>(nw) * G * d.head_dim * 4 <= kSkMergeLds;
   if (S > 1 || sk) {
     char* ws = static_cast<char*>(a.workspace);
@@ -822,9 +741,7 @@ int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream) {
   const int grid = static_cast<int>(grid64);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int key = (d.head_dim == 128 ? 4 : 0) | (d.block_size == 128 ? 2 : 0) | (dense ? 1 : 0);
-  if (sel)
-    nw == 8 ? launch_variant_sel<8>(key, p, grid, s) : launch_variant_sel<4>(key, p, grid, s);
-  else if (sk)
+  if (sk)
     nw == 8 ? launch_variant_sk<8>(key, p, grid, s) : launch_variant_sk<4>(key, p, grid, s);
   else if (nw == 8)
     paged ? launch_variant<8, true>(key, p, grid, s) : launch_variant<8, false>(key, p, grid, s);

@@ -142,7 +142,6 @@ struct GateParams {
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
   float* logits_out;   // [B, H_kv, NBmax] or null
-  int32_t* scored_out; // [B, H_kv]: the number of scored blocks, or null
   int32_t* block_idx;  // select when non-null (one row part only)
   int32_t* num_selected;
   int pairs;           // B * H_kv; workgroup = part * pairs + pair
@@ -249,7 +248,6 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   const int nnew = max(0, min(nc, r1) - e0);
   select_smem_init(s_sel);
   const double wf = rope_freq(tid % (DG / 2), DG, p.log2_theta);
-  if (part == 0 && p.scored_out != nullptr && tid == 0) p.scored_out[pair] = nc;
 
   // ---- new cache entries (blocks completed since the last update), in one
   // pass before anything else is in flight (they are rare: one step in b)
@@ -443,7 +441,6 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   p.kcomp_lens = a.kcomp_lens;
   p.seq_lens = a.seq_lens;
   p.logits_out = a.logits_out;
-  p.scored_out = a.scored_out;
   p.block_idx = a.block_idx;
   p.num_selected = a.num_selected;
   const int64_t pairs = static_cast<int64_t>(d.batch) * d.num_kv_heads;

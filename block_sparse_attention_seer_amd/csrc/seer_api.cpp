@@ -206,23 +206,13 @@ static int check_paged(const seer_dims* dims, const PagedCache& pc, std::string*
   return SEER_OK;
 }
 
-// Selection inside the decode launch (fused step): where the gate launch
-// left the block logits and scored counts, and the selection rule.
-struct DecodeSelect {
-  const float* logits;
-  const int32_t* scored;
-  int mode, topk;
-  float tau;
-};
-
 static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* seq_lens, const int32_t* block_idx,
                          const int32_t* num_selected, int32_t max_blocks, float scale,
                          int32_t num_split, void* workspace, size_t workspace_bytes,
                          uint16_t* out, float* lse, void* stream,
                          int32_t* commit_lens = nullptr, int commit_max_new = 0,
-                         const PagedCache* paged = nullptr, bool stream_k = false,
-                         const DecodeSelect* select = nullptr) {
+                         const PagedCache* paged = nullptr, bool stream_k = false) {
   SEER_CHECK(check_dims(dims, &why_));
   SEER_CHECK(check_ptr(q, 16, "q", &why_));
   SEER_CHECK(check_ptr(k, 16, "k_cache", &why_));
@@ -252,15 +242,6 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
   seer::DecodeArgs a{q, k, v, seq_lens, block_idx, num_selected, max_blocks, scale, s,
                      workspace, out, lse, commit_lens, commit_max_new};
   a.stream_k = stream_k;
-  if (select != nullptr) {
-    a.sel_logits = select->logits;
-    a.sel_scored = select->scored;
-    a.sel_block_idx = const_cast<int32_t*>(block_idx);
-    a.sel_num_selected = const_cast<int32_t*>(num_selected);
-    a.sel_mode = select->mode;
-    a.sel_topk = select->topk;
-    a.sel_tau = select->tau;
-  }
   if (paged != nullptr) {
     SEER_CHECK(check_paged(dims, *paged, &why_));
     a.block_table = paged->block_table;
@@ -387,19 +368,10 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   if (max_new_blocks > seer::nb_max(dims)) max_new_blocks = static_cast<int32_t>(seer::nb_max(dims));
 
   // Launch 1: per (b, h), the entries of newly completed blocks, the gate
-  // query and the logits.  Launch 2: the sparse decode, which also raises
-  // kcomp_lens over those entries.  The selection runs at the end of launch
-  // 1 when launch 2 is stream-K (it needs every pair's count up front) or
-  // cannot select with the select kernel's thread count; otherwise at the
-  // start of launch 2, so that launch 1 only scores and can spread each
-  // pair's cache rows over several workgroups.  More new blocks than one
+  // query, the logits and the selection.  Launch 2: the sparse decode, which
+  // also raises kcomp_lens over those entries.  More new blocks than one
   // gate launch computes (a catch-up after a prompt) take the staged update
   // first.
-  const int dec_waves = seer::decode_waves_per_group(g, dims->head_dim);
-  const bool select_in_decode =
-      !stream_k && (mode == SEER_SELECT_TOPK || dec_waves == 8) &&
-      std::max<int64_t>(static_cast<int64_t>(dec_waves) * g * dims->head_dim, seer::nb_max(dims)) +
-              max_selected <= seer::kSelDecodeWords;
   int rc = SEER_OK;
   int inline_new = max_new_blocks;
   if (max_new_blocks > seer::kMaxInlineNew) {
@@ -431,25 +403,18 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   ga.kcomp = kcomp;
   ga.kcomp_lens = kcomp_lens;
   ga.seq_lens = seq_lens;
-  float* const ws_logits = reinterpret_cast<float*>(ws + seer::step_gate_query_bytes(dims));
-  int32_t* const ws_scored = reinterpret_cast<int32_t*>(ws + seer::step_gate_query_bytes(dims) +
-                                                        seer::step_gate_logits_bytes(dims));
-  ga.logits_out = select_in_decode ? (logits != nullptr ? logits : ws_logits) : logits;
-  ga.scored_out = ws_scored;
-  ga.block_idx = select_in_decode ? nullptr : block_idx;
+  ga.logits_out = logits;
+  ga.block_idx = block_idx;
   ga.num_selected = num_selected;
-  ga.row_parts = select_in_decode ? gate_row_parts(dims) : 1;
   ga.mode = mode;
   ga.topk = topk_blocks;
   ga.max_selected = max_selected;
   ga.tau = threshold;
   rc = seer::launch_gate(*dims, ga, stream);
   if (rc != SEER_OK) return rc;
-  const DecodeSelect sel{ga.logits_out, ws_scored, mode, topk_blocks, threshold};
   return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,
                        scale, s, ws + seer::step_gate_bytes(dims), dec_bytes, out, lse, stream,
-                       inline_new > 0 ? kcomp_lens : nullptr, inline_new, nullptr, stream_k,
-                       select_in_decode ? &sel : nullptr);
+                       inline_new > 0 ? kcomp_lens : nullptr, inline_new, nullptr, stream_k);
 }
 
 size_t seer_prefill_workspace_bytes(const seer_dims* dims) {

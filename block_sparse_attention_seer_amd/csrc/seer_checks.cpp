@@ -94,19 +94,8 @@ size_t gate_workspace_bytes(const seer_dims* d) {
   return static_cast<size_t>(d->batch) * d->num_kv_heads * d->d_gate * sizeof(float);
 }
 
-namespace {
-size_t round_up(size_t n) { return (n + kCounterBytes - 1) / kCounterBytes * kCounterBytes; }
-}  // namespace
-
-size_t step_gate_query_bytes(const seer_dims* d) { return round_up(gate_workspace_bytes(d)); }
-
-size_t step_gate_logits_bytes(const seer_dims* d) {
-  return round_up(static_cast<size_t>(d->batch) * d->num_kv_heads * nb_max(d) * sizeof(float));
-}
-
 size_t step_gate_bytes(const seer_dims* d) {
-  const size_t scored = round_up(static_cast<size_t>(d->batch) * d->num_kv_heads * sizeof(int32_t));
-  return step_gate_query_bytes(d) + step_gate_logits_bytes(d) + scored;
+  return (gate_workspace_bytes(d) + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
 }
 
 size_t decode_workspace_bytes(int64_t pairs, int num_split, int g, int head_dim) {

@@ -20,8 +20,6 @@ constexpr int kCounterBytes = 256;     // alignment of the partial outputs after
 constexpr int kPrefillTokenTile = 64;  // prefill: key tile, and the padding of the token axis
 constexpr int kSkMaxPairs = 2048;      // (b, h) pairs the stream-K decode prefixes in LDS
 constexpr int kSkMergeLds = 32 * 1024; // wave-merge LDS bytes that leave room for that prefix
-constexpr int kSelDecodeWords = 12288; // LDS words of a decode launch that selects: max(wave
-                                       // merge, NBmax keys) + the max_selected index row
 constexpr int kMaxGateParts = 4;       // workgroups per (b, h) in a scoring-only gate launch
 
 // ------------------------------------------------------- argument checks
@@ -34,12 +32,7 @@ int check_ptr(const void* p, size_t align, const char* name, std::string* why);
 
 int64_t nb_max(const seer_dims* d);  // ceil(Lmax / b)
 size_t gate_workspace_bytes(const seer_dims* d);
-// The gate's part of the fused step's workspace (it comes first), each piece
-// rounded up to 256 bytes: the gate queries [B, H_kv, d_gate] float32, the
-// block logits [B, H_kv, NBmax] float32 (when the caller keeps none), the
-// scored block counts [B, H_kv] int32.
-size_t step_gate_query_bytes(const seer_dims* d);
-size_t step_gate_logits_bytes(const seer_dims* d);
+// The gate queries inside the fused step's workspace, rounded up to 256 bytes.
 size_t step_gate_bytes(const seer_dims* d);
 // Workspace of the decode kernel for `pairs` (b, h) pairs, `num_split`
 // splits and group size g: the per-split lse and outputs.
@@ -87,7 +80,6 @@ struct GateArgs {
   const int32_t* kcomp_lens;
   const int32_t* seq_lens;
   float* logits_out;       // or nullptr
-  int32_t* scored_out;     // [B, H_kv] scored block counts, or nullptr
   int32_t* block_idx;      // selection when non-null (then one row part)
   int32_t* num_selected;
   int mode, topk, max_selected;
@@ -137,16 +129,6 @@ struct DecodeArgs {
   // decode_sk_workspace_bytes(); the launch falls back to fixed splits where
   // the stream-K kernel does not apply.
   bool stream_k = false;
-  // Select in this launch from the gate launch's logits [pairs, NBmax] and
-  // scored counts [pairs] (sel_logits non-null; block_idx / num_selected
-  // above are then ignored and the selection is written to sel_block_idx /
-  // sel_num_selected); contiguous cache and fixed splits only.
-  const float* sel_logits = nullptr;
-  const int32_t* sel_scored = nullptr;
-  int32_t* sel_block_idx = nullptr;
-  int32_t* sel_num_selected = nullptr;
-  int sel_mode = 0, sel_topk = 0;
-  float sel_tau = 0.f;
 };
 int launch_decode(const seer_dims& d, const DecodeArgs& a, void* stream);
 

@@ -820,6 +820,8 @@ def _clone_state(st_from, st_to):
     ("threshold_b128", dict(batch=6, max_seq_len=20000, seq_len_range=(3000, 20000))),
     ("qwen3_14b_b16", dict(batch=3, mode="topp", tau=0.6)),
     ("tiny", dict(seq_len=1000, mode="topp", tau=0.8)),
+    # 16 query heads per KV head: 4-wave decode workgroups
+    ("qwen3_14b_b16", dict(batch=3, num_q_heads=32, num_kv_heads=2)),
 ])
 def test_fused_step_equals_staged(S, name, overrides):
     """seer_decode_step reproduces the four staged calls bit for bit.  Under
@@ -870,6 +872,41 @@ def test_fused_step_equals_staged(S, name, overrides):
              else [(w.batch - 1, w.num_kv_heads - 1)])
     for bb, hh in pairs:
         _check_pair(w, inp, b, bb, hh, f"fused {name} b={bb} h={hh}")
+
+
+def test_fused_step_long_row(S):
+    """Rows of 100k to 147k tokens (2304 blocks per row, threshold, two fixed
+    splits): cache, indices, logits and outputs of the fused step equal the
+    staged calls bit for bit; one pair per sequence against the oracle."""
+    w = WORKLOADS["pipeline_128k"].replace(batch=2, max_seq_len=147456,
+                                           seq_len_range=(100000, 147000), mode="threshold",
+                                           tau=0.002)
+    say("fused step, long row")
+    inp = make_inputs(w, device=DEV, separate_nope=True)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    kw = dict(mode=MODES["threshold"], threshold=w.tau, num_split=2, device=DEV)
+    fused = S.DecodeStep(dims, **kw)
+    staged = S.DecodeStep(dims, **kw)
+    seq = inp["seq_lens"]
+    fused.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - 1, min=0))
+    _clone_state(fused, staged)
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    fused.fused_step(*args)
+    staged.step(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.kcomp_lens, staged.kcomp_lens)
+    assert torch.equal(fused.kcomp, staged.kcomp)
+    assert torch.equal(fused.num_selected, staged.num_selected)
+    assert torch.equal(fused.block_idx, staged.block_idx)
+    assert torch.equal(fused.logits, staged.logits)
+    assert torch.equal(fused.out.view(torch.int16), staged.out.view(torch.int16))
+    assert torch.equal(fused.lse.view(torch.int32), staged.lse.view(torch.int32))
+    assert int(step_decode_counters(fused).abs().sum()) == 0
+    for b in range(w.batch):
+        _check_pair(w, inp, fused, b, b % w.num_kv_heads, f"long row b={b}")
+    del inp
+    torch.cuda.empty_cache()
 
 
 SK_CASES = [
