@@ -19,7 +19,11 @@ kept, 16 replicas measured 0.5 us per step faster, 24 and 32 the same.
 Prints one JSON line: µs per step (lower is better), achieved HBM bandwidth
 of the decode kernel on its algorithmic bytes against the 8 TB/s peak, the
 speedup over the library's own dense decode at equal shape, and the float64
-oracle timed on the host cores on a bounded sample.  The line also carries
+oracle's whole step timed on the host cores.  Its "extra" object holds the
+other configurations (step, decode and dense µs, GB/s, fraction of peak and
+speedup each): the Qwen3-8B-shaped layer at batch 1, the 64-sequence
+threshold batch, the 256-step 128k pipeline, the benchmarked batch over a
+paged cache and with top-p 0.9 and 0.99 (--no-extra leaves it out).  The line also carries
 the training-side call, seer_prefill_attention (causal prefill forward with
 the gate's ground truth) on a 32k-token Qwen3-14B-shaped layer, against the
 2.5 PFLOP/s dense bf16 MFMA peak ("prefill_gt"; --prefill-only runs just
@@ -90,13 +94,16 @@ def main() -> int:
     ap.add_argument("--mass", type=float, default=0.9,
                     help="threshold tau or top-p mass p when --select overrides the rule")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="budget of the oracle CPU baseline (the whole step when it fits)")
     ap.add_argument("--flushed-iters", type=int, default=100,
                     help="iterations of the per-iteration timing with a 1 GiB cache flush "
                          "(0 skips it)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only seer_prefill_attention and print its object")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave the other configurations out of the headline line")
     ap.add_argument("--extra", action="store_true",
                     help="instead of the headline line: one JSON line each for the Qwen3-8B-shaped "
                          "layer, the 64-sequence threshold batch, the 256-step 128k pipeline, "
@@ -216,6 +223,8 @@ def main() -> int:
     # same replicas and the selections the steps just made
     # (the binding launches on torch's current stream, which these events see)
     log(f"timing {args.steps} decode launches")
+    for i in range(3):  # the standalone decode kernel's first launches (code loading) untimed
+        decode_only(i % R)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -377,6 +386,17 @@ def main() -> int:
         "cpu_baseline": cpu,
         "prefill_gt": prefill,
     }
+    if not args.no_extra:
+        # the other configurations, after the headline's replicas are freed
+        del reps, bound, graphs, inp0, st0, dws, dout, dlse
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        t_extra = time.perf_counter()
+        line["extra"] = {}
+        for key, obj in extra_measurements(S, torch, np, dev, grid=False):
+            line["extra"][key] = obj
+        log(f"extra configurations took {time.perf_counter() - t_extra:.1f} s")
     print(json.dumps(line), flush=True)
     return 0
 
@@ -469,10 +489,23 @@ def traffic_pass(reps, decode_only, torch, dev, L, bs, d):
     return 0
 
 
-def cpu_baseline(inp, w, budget_s):
+def blas_threads():
+    """Threads of the BLAS library NumPy calls (None if it cannot be asked)."""
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:
+        return None
+    n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+    return max(n) if n else None
+
+
+def cpu_baseline(inp, w, budget_s, repeats=3):
     """The float64 oracle's decode step (gate query, logits, selection,
-    attention; its cache prebuilt and untimed) on sampled (b, h) pairs,
-    scaled to µs per full step."""
+    attention) over every (b, h) pair of the batch: each pair's cache is built
+    untimed, then its decode is timed `repeats` times and the median kept; the
+    step is the sum of the pairs' medians.  Pairs go in a seeded random order;
+    if the budget runs out first, the mean of the timed pairs is scaled to the
+    whole batch (the line says how many pairs were timed)."""
     import numpy as np
 
     import oracle as O
@@ -481,42 +514,41 @@ def cpu_baseline(inp, w, budget_s):
     L = w.seq_len
     g = w.group
     pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(pairs))
-    log("cpu baseline: preparing sampled pairs")
-    prepared = []
-    t_prep = time.perf_counter()
-    for i in order[:8]:
-        b, h = pairs[i]
-        k = f(inp["k"][b, h, :L])
-        kc = O.build_kcomp(k, f(inp["w_k"][h]), L, w.block_size, w.theta)
-        prepared.append((f(inp["q"][b, h * g:(h + 1) * g]), k, f(inp["v"][b, h, :L]),
-                         f(inp["w_q"][h]), kc))
-        if time.perf_counter() - t_prep > budget_s:
-            break
-    times = []
+    order = np.random.default_rng(0).permutation(len(pairs))
+    log(f"cpu baseline: {len(pairs)} pairs, budget {budget_s:.0f} s")
+    medians = []
     t_start = time.perf_counter()
-    n = 0
-    while True:
-        q, k, v, wq, kc = prepared[n % len(prepared)]
-        t0 = time.perf_counter()
-        O.decode_pair(q, q, k, k, v, wq, kc, L, w.block_size, mode=w.mode, topk=w.topk_blocks,
-                      tau=w.tau, scale=1.0 / math.sqrt(w.head_dim), theta=w.theta)
-        times.append(time.perf_counter() - t0)
-        n += 1
-        if time.perf_counter() - t_start > budget_s and n >= len(prepared):
+    for i in order:
+        b, h = pairs[i]
+        q = f(inp["q"][b, h * g:(h + 1) * g])
+        k, v = f(inp["k"][b, h, :L]), f(inp["v"][b, h, :L])
+        kc = O.build_kcomp(k, f(inp["w_k"][h]), L, w.block_size, w.theta)
+        wq = f(inp["w_q"][h])
+        times = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            O.decode_pair(q, q, k, k, v, wq, kc, L, w.block_size, mode=w.mode, topk=w.topk_blocks,
+                          tau=w.tau, scale=1.0 / math.sqrt(w.head_dim), theta=w.theta)
+            times.append(time.perf_counter() - t0)
+        medians.append(float(np.median(times)))
+        if time.perf_counter() - t_start > budget_s:
             break
-    per_pair = float(np.median(times))
+    full = len(medians) == len(pairs)
+    value = sum(medians) if full else float(np.mean(medians)) * len(pairs)
     try:
-        cores = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count()
-    return {"value": round(per_pair * len(pairs) * 1e6, 1), "unit": "us/step", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{n} oracle pair-steps over {len(prepared)} sampled (b, h) pairs of "
-                      f"{len(pairs)}; median pair time x {len(pairs)} pairs; NumPy float64, "
-                      f"BLAS threads at default"}
-
+        affinity = os.cpu_count()
+    threads = blas_threads()
+    return {"value": round(value * 1e6, 1), "unit": "us/step",
+            "cores": threads if threads is not None else affinity, "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas_threads": threads,
+            "pairs_timed": len(medians), "pairs": len(pairs),
+            "sample": (f"the whole step: all {len(pairs)} (b, h) pairs, each pair's decode "
+                       f"timed {repeats} times (median), summed" if full else
+                       f"{len(medians)} of {len(pairs)} (b, h) pairs in a seeded random order, "
+                       f"each timed {repeats} times (median); mean pair time x {len(pairs)}")
+            + "; caches built untimed; NumPy float64, BLAS threads at default"}
 
 
 # ----------------------------------------------------------------- --extra
@@ -574,8 +606,11 @@ def _selected_tokens(st, lens, bs):
     return tot
 
 
-def extra_lines(S, torch, np, dev):
-    """Measurements beyond the headline configuration, one JSON line each."""
+def extra_measurements(S, torch, np, dev, grid=False):
+    """Measurements beyond the headline configuration: yields (key, object)
+    for the Qwen3-8B-shaped layer, the 64-sequence threshold batch, the
+    256-step 128k pipeline, the benchmarked batch over a paged cache and with
+    top-p 0.9 / 0.99, and (grid=True) the pages' microbenchmark grid."""
     from workloads import WORKLOADS, make_inputs
     modes = {"topk": S.SELECT_TOPK, "threshold": S.SELECT_THRESHOLD}
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -631,7 +666,7 @@ def extra_lines(S, torch, np, dev):
         dec_alg = sel * 2 * d * 2 + qo + idx_bytes
         step_alg = dec_alg + sum(int(L) // bs for L in lens) * Hkv * dg * 2 + Hkv * dg * (Hq // Hkv) * d * 2
         dense_bytes = int(lens.sum()) * Hkv * 2 * d * 2 + qo
-        print(json.dumps({
+        yield name, {
             "kind": "config", "workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
             "head_dim": d, "block_size": bs, "mode": w.mode,
             "seq_len": int(lens[0]) if w.seq_len else [int(lens.min()), int(lens.max())],
@@ -646,7 +681,7 @@ def extra_lines(S, torch, np, dev):
             "speedup_vs_dense_kernel": round(dense_us / dec_us, 3),
             "selected_fraction": round(sel / float(lens.sum() * Hkv), 4),
             "timing": "event pair around back-to-back launches, two input replicas alternating",
-        }), flush=True)
+        }
         del reps
         torch.cuda.empty_cache()
 
@@ -670,19 +705,28 @@ def extra_lines(S, torch, np, dev):
         times.append(_events_us(torch, lambda i: runs[i](), w.steps))
     l0 = L0.cpu().numpy().astype(np.int64)
     completions = int(((l0 + w.steps) // bs - l0 // bs).sum())
+    # algorithmic bytes of the last step (its selections are still in st)
+    l_last = lens[-1].cpu().numpy().astype(np.int64)
+    g_ = Hq // Hkv
+    last_alg = (_selected_tokens(st, l_last, bs) * 2 * d * 2 + 2 * B * Hq * d * 2
+                + B * Hkv * (st.max_selected + 1) * 4 + int((l_last // bs).sum()) * Hkv * dg * 2
+                + Hkv * dg * g_ * d * 2)
     dn = _dense_buffers(S, torch, dims, dev)
     dense_last = _events_us(torch, lambda i: S.seer_dense_decode(
         dims, inp["q"], inp["k"], inp["v"], lens[-1], scale, *dn), 5)
-    print(json.dumps({
+    yield "pipeline_128k", {
         "kind": "pipeline", "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
         "head_dim": d, "block_size": bs, "topk_blocks": w.topk_blocks, "steps": w.steps,
         "start_len": [int(l0.min()), int(l0.max())],
         "us_per_step": round(times[1], 2), "block_completions": completions,
+        "step_GBps_last_step_bytes": round(last_alg / (times[1] * 1e-6) / 1e9, 1),
+        "step_frac_of_peak_last_step_bytes": round(last_alg / (times[1] * 1e-6) / 1e9 / PEAK_GBPS,
+                                                   4),
         "dense_us_at_last_length": round(dense_last, 2),
         "speedup_vs_dense_step": round(dense_last / times[1], 3),
         "timing": "event pair around the 256 fused steps (cache update, gate, selection, "
                   "decode), after one untimed pass from the same start",
-    }), flush=True)
+    }
     del inp, st, runs
     torch.cuda.empty_cache()
 
@@ -746,7 +790,7 @@ def extra_lines(S, torch, np, dev):
     blocks = int(st.num_selected.sum().item())
     qo = 2 * B * Hq * d * 2
     alg = sel * 2 * d * 2 + qo + B * Hkv * (st.max_selected + 1) * 4
-    print(json.dumps({
+    yield "qwen3_14b_b16_paged", {
         "kind": "paged", "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
         "head_dim": d, "block_size": bs, "seq_len": int(lens[0]), "pages": B * nbm,
         "sparse_decode_us": round(t["dec"], 2), "sparse_decode_paged_us": round(t["dec_paged"], 2),
@@ -754,9 +798,10 @@ def extra_lines(S, torch, np, dev):
         "sparse_paged_frac_of_peak": round((alg + 4 * blocks) / (t["dec_paged"] * 1e-6) / 1e9
                                            / PEAK_GBPS, 4),
         "dense_decode_us": round(t["dense"], 2), "dense_decode_paged_us": round(t["dense_paged"], 2),
+        "speedup_vs_dense_kernel_paged": round(t["dense_paged"] / t["dec_paged"], 3),
         "paged_equals_contiguous": same and same_dense,
         "timing": "median of per-launch event pairs, 1 GiB read before each",
-    }), flush=True)
+    }
     del kp, vp, table, perm_d
 
     # top-p over the same inputs: the fused step (whose decode divides the
@@ -778,7 +823,7 @@ def extra_lines(S, torch, np, dev):
         dec_us = _flushed_median_us(torch, dec_p, 30, flush)
         sel_p = _selected_tokens(stp, lens, bs)
         alg_p = sel_p * 2 * d * 2 + qo + B * Hkv * (stp.max_selected + 1) * 4
-        print(json.dumps({
+        yield f"qwen3_14b_b16_topp_{p_mass}", {
             "kind": "topp", "workload": w.name, "p": p_mass, "batch": B, "q_heads": Hq,
             "kv_heads": Hkv, "seq_len": int(lens[0]),
             "step_us": round(step_us, 2), "decode_fixed_splits_us": round(dec_us, 2),
@@ -789,11 +834,14 @@ def extra_lines(S, torch, np, dev):
             "dense_decode_us": round(t["dense"], 2),
             "speedup_vs_dense_step": round(t["dense"] / step_us, 3),
             "timing": "median of per-launch event pairs, 1 GiB read before each",
-        }), flush=True)
+        }
         del stp
     del inp, st, run_topk, dn
     torch.cuda.empty_cache()
 
+    if not grid:
+        del flush
+        return
     # ---- the pages' microbenchmark grid: kernel-level sparse vs dense
     base = WORKLOADS["qwen3_8b_layer"]
     for B in (1, 4, 16):
@@ -827,19 +875,26 @@ def extra_lines(S, torch, np, dev):
                 de_us = _flushed_median_us(torch, dense, 10, flush)
                 sel = _selected_tokens(st, inp["seq_lens"].cpu().numpy(), 64)
                 alg = sel * 2 * 128 * 2 + 2 * B * 64 * 128 * 2 + B * 8 * (st.max_selected + 1) * 4
-                print(json.dumps({
+                yield f"grid_b{B}_l{L}_s{sp}", {
                     "kind": "grid", "batch": B, "q_heads": 64, "kv_heads": 8, "head_dim": 128,
                     "block_size": 64, "seq_len": L, "sparsity": sp, "topk_blocks": k,
                     "sparse_decode_us": round(sp_us, 2), "dense_decode_us": round(de_us, 2),
                     "speedup_kernel": round(de_us / sp_us, 3),
                     "sparse_GBps": round(alg / (sp_us * 1e-6) / 1e9, 1),
                     "timing": "median of per-launch event pairs, 1 GiB read before each",
-                }), flush=True)
+                }
                 del st
             del inp
             torch.cuda.empty_cache()
     del flush
+
+
+def extra_lines(S, torch, np, dev):
+    """--extra: every extra measurement, the grid included, one JSON line each."""
+    for _, obj in extra_measurements(S, torch, np, dev, grid=True):
+        print(json.dumps(obj), flush=True)
     return 0
+
 
 if __name__ == "__main__":
     sys.exit(main())

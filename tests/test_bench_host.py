@@ -57,26 +57,47 @@ def test_decode_src_hash_tracks_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.decode_src_hash() != h0
 
 
-def test_cpu_baseline_scales_the_median_pair_time(monkeypatch):
-    """value = median oracle time of one (b, h) pair x the number of pairs;
-    the oracle call is replaced by a fixed 2 ms sleep to check the scaling."""
+def _fixed_oracle(monkeypatch, seconds):
     import time
 
     import oracle
-
-    from workloads import WORKLOADS, make_inputs
-    w = WORKLOADS["tiny"].replace(batch=3)
-    inp = make_inputs(w, device="cpu")
     calls = []
 
     def fixed(*a, **k):
         calls.append(k.get("mode"))
-        time.sleep(0.002)
+        time.sleep(seconds)
 
     monkeypatch.setattr(oracle, "decode_pair", fixed)
-    res = bench.cpu_baseline(inp, w, 0.1)
+    return calls
+
+
+def test_cpu_baseline_sums_every_pair(monkeypatch):
+    """Within the budget the value is the whole step: every (b, h) pair timed
+    three times, the medians summed.  The oracle call is replaced by a fixed
+    2 ms sleep to check the arithmetic."""
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["tiny"].replace(batch=3)
+    inp = make_inputs(w, device="cpu")
+    calls = _fixed_oracle(monkeypatch, 0.002)
+    res = bench.cpu_baseline(inp, w, 60.0)
     pairs = w.batch * w.num_kv_heads
     assert res["kind"] == "oracle" and res["unit"] == "us/step" and res["cores"] >= 1
+    assert res["pairs_timed"] == res["pairs"] == pairs
+    assert len(calls) == 3 * pairs and all(m == w.mode for m in calls)
     assert 2000 * pairs <= res["value"] <= 3000 * pairs
-    assert calls and all(m == w.mode for m in calls)
-    assert f"of {pairs};" in res["sample"]
+    assert res["os_cpu_count"] == os.cpu_count() and res["affinity_cpus"] >= 1
+    assert "the whole step" in res["sample"]
+
+
+def test_cpu_baseline_scales_a_cut_sample(monkeypatch):
+    """A budget too small for every pair: the mean of the timed pairs times
+    the number of pairs, and the line names how many were timed."""
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["tiny"].replace(batch=5)
+    inp = make_inputs(w, device="cpu")
+    _fixed_oracle(monkeypatch, 0.002)
+    res = bench.cpu_baseline(inp, w, 0.0)  # stops after the first pair
+    pairs = w.batch * w.num_kv_heads
+    assert res["pairs_timed"] == 1 < pairs
+    assert 2000 * pairs <= res["value"] <= 3000 * pairs
+    assert f"1 of {pairs}" in res["sample"]
