@@ -144,6 +144,8 @@ struct GateParams {
   float* logits_out;   // [B, H_kv, NBmax] or null
   int32_t* block_idx;  // select when non-null (one row part only)
   int32_t* num_selected;
+  int32_t* clear_ctr;  // [B * H_kv] split counters of the decode launch after this one, set
+                       // to zero here (fused step), or null
   int pairs;           // B * H_kv; workgroup = part * pairs + pair
   int rows_per_part;   // logit rows of one workgroup (a multiple of 64)
   int Hq, Hkv, G, BS, Lmax, NBmax;
@@ -243,6 +245,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   int nc0 = p.kcomp_lens[b];
   nc0 = min(min(max(nc0, 0), p.NBmax), L / p.BS);  // cached blocks
   const int nc = min(L / p.BS, nc0 + p.max_new);   // scored: with this launch's entries
+  if (p.clear_ctr != nullptr && part == 0 && tid == 0) p.clear_ctr[pair] = 0;
   // this launch's new entries that fall in this workgroup's rows
   const int e0 = max(nc0, r0);
   const int nnew = max(0, min(nc, r1) - e0);
@@ -443,6 +446,7 @@ int launch_gate(const seer_dims& d, const GateArgs& a, void* stream) {
   p.logits_out = a.logits_out;
   p.block_idx = a.block_idx;
   p.num_selected = a.num_selected;
+  p.clear_ctr = a.clear_counters;
   const int64_t pairs = static_cast<int64_t>(d.batch) * d.num_kv_heads;
   p.pairs = static_cast<int>(pairs);
   p.Hq = d.num_q_heads;

@@ -410,6 +410,10 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   ga.topk = topk_blocks;
   ga.max_selected = max_selected;
   ga.tau = threshold;
+  // the decode's split counters (at the start of its workspace) are zeroed
+  // by the gate launch, so the workspace needs no particular contents
+  if (s > 1 || stream_k)
+    ga.clear_counters = reinterpret_cast<int32_t*>(ws + seer::step_gate_bytes(dims));
   rc = seer::launch_gate(*dims, ga, stream);
   if (rc != SEER_OK) return rc;
   return decode_common(dims, q, k_cache, v_cache, seq_lens, block_idx, num_selected, max_selected,

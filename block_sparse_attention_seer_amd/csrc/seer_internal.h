@@ -85,6 +85,7 @@ struct GateArgs {
   int mode, topk, max_selected;
   float tau;
   int row_parts = 1;       // workgroups per (b, h), each scoring a range of cache rows
+  int32_t* clear_counters = nullptr;  // [B * H_kv] decode split counters to zero, or nullptr
 };
 int launch_gate(const seer_dims& d, const GateArgs& a, void* stream);
 

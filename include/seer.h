@@ -25,9 +25,11 @@
  *   - The caller owns every buffer.  The library allocates nothing and keeps
  *     no pointer after a call returns.  Outputs are fully overwritten
  *     (including padding), so callers never pre-initialise them; the only
- *     exceptions are the decode and fused-step workspaces, which hold
- *     counters and must be zero-filled once before their first use (every
- *     call leaves the counters zero again).
+ *     exception is the decode workspace of
+ *     seer_sparse_decode / seer_dense_decode (and their paged forms), which
+ *     holds counters that must be zero before it is first used (every call
+ *     leaves them zero again).  The fused step's workspace needs no
+ *     particular contents.
  *   - Host-detectable errors return before anything is launched; nothing is
  *     written.  A kernel launch failure returns SEER_ERR_HIP.  Device-side
  *     data problems cannot be reported synchronously: out-of-range lengths
@@ -199,8 +201,10 @@ int seer_select_blocks(const seer_dims* dims, const float* logits,
  * (queries the current device).
  * The counters must be ZERO before the first call that uses a workspace;
  * every call leaves them zero again, so one zero-fill at allocation is
- * enough.  One workspace must not be used by two calls that can run at the
- * same time.
+ * enough while the workspace serves calls of at most as many (b, h) pairs
+ * as the first (the counters are the first B * H_kv words; a call with
+ * more pairs finds partial results there: zero it again first).  One
+ * workspace must not be used by two calls that can run at the same time.
  */
 size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks,
                                    int32_t num_split);
@@ -330,10 +334,10 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
  *                    writing them.
  *   scale, num_split as seer_sparse_decode.
  *   workspace        >= seer_decode_step_workspace_bytes(dims, max_selected,
- *                    num_split) bytes, 256-byte aligned: the gate workspace
- *                    (rounded up to 256 bytes), then the decode workspace;
- *                    both hold counters, so zero-fill the whole workspace
- *                    before its first use (every call leaves them zero).
+ *                    num_split) bytes, 256-byte aligned, no initial contents
+ *                    needed: the gate queries (rounded up to 256 bytes), then
+ *                    the decode workspace, whose split counters launch 1
+ *                    zeroes.  One workspace may serve calls of any sizes.
  *                    With num_split = 0 the size includes the stream-K
  *                    decode's per-workgroup partials; a workspace sized for
  *                    the split decode alone is still accepted (no stream-K).

@@ -874,6 +874,39 @@ def test_fused_step_equals_staged(S, name, overrides):
         _check_pair(w, inp, b, bb, hh, f"fused {name} b={bb} h={hh}")
 
 
+@pytest.mark.parametrize("name,overrides", [
+    ("qwen3_14b_b16", dict(batch=4)),  # fixed splits
+    ("threshold_b128", dict(batch=6, max_seq_len=20000, seq_len_range=(3000, 20000))),  # stream-K
+])
+def test_fused_step_needs_no_workspace_contents(S, name, overrides):
+    """The fused step over a workspace filled with a garbage pattern (every
+    word 0x7fc00000, counters included) gives the bits it gives over a
+    zero-filled one: the gate launch zeroes the decode's split counters,
+    and the decode leaves them zero."""
+    w = WORKLOADS[name].replace(**overrides)
+    say(f"fused step over a garbage workspace: {name} {overrides}")
+    inp = make_inputs(w, device=DEV, separate_nope=True)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    kw = dict(mode=MODES[w.mode], topk_blocks=w.topk_blocks, threshold=w.tau, device=DEV)
+    clean, dirty = S.DecodeStep(dims, **kw), S.DecodeStep(dims, **kw)
+    seq = inp["seq_lens"]
+    clean.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - w.block_size, min=0))
+    _clone_state(clean, dirty)
+    dirty.step_ws.view(torch.int32).fill_(0x7fc00000)
+    assert clean.num_split > 1 or w.mode != "topk"  # the decode uses its counters
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    clean.fused_step(*args)
+    dirty.fused_step(*args)
+    torch.cuda.synchronize()
+    for name_ in ("kcomp_lens", "kcomp", "num_selected", "block_idx", "logits"):
+        assert torch.equal(getattr(clean, name_), getattr(dirty, name_)), name_
+    assert torch.equal(clean.out.view(torch.int16), dirty.out.view(torch.int16))
+    assert torch.equal(clean.lse.view(torch.int32), dirty.lse.view(torch.int32))
+    assert int(step_decode_counters(dirty).abs().sum()) == 0
+    _check_pair(w, inp, dirty, w.batch - 1, w.num_kv_heads - 1, f"garbage workspace {name}")
+
+
 def test_fused_step_long_row(S):
     """Rows of 100k to 147k tokens (2304 blocks per row, threshold, two fixed
     splits): cache, indices, logits and outputs of the fused step equal the
