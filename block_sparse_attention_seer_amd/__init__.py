@@ -36,7 +36,8 @@ __all__ = [
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
     "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
     "seer_decode_step_workspace_bytes",
-    "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
+    "seer_decode_step", "seer_decode_step_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "seer_status_string", "seer_last_error_message", "seer_version",
     "DecodeStep",
 ]
 
@@ -47,6 +48,7 @@ SEER_OK = 0
 SELECT_TOPK = 1
 SELECT_THRESHOLD = 2
 SELECT_TOPP = 3  # threshold carries the mass p
+NOALLOC_SCRATCH_BYTES = 16 << 20  # seer_decode_step_noalloc's static workspace per GPU
 
 EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
@@ -55,7 +57,8 @@ EXPORTED_SYMBOLS = (
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
     "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
     "seer_decode_step_workspace_bytes",
-    "seer_decode_step", "seer_status_string", "seer_last_error_message", "seer_version",
+    "seer_decode_step", "seer_decode_step_noalloc", "seer_status_string",
+    "seer_last_error_message", "seer_version",
 )
 
 
@@ -118,6 +121,10 @@ _SIGS = {
     "seer_decode_step": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _I32, ctypes.c_double, _I32, _I32, ctypes.c_float, _I32, _P, _P,
                                 _P, ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
+    "seer_decode_step_noalloc": (_I32, [ctypes.POINTER(SeerDims), _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _I32, ctypes.c_double, _I32, _I32,
+                                        ctypes.c_float, _I32, _P, _P, _P, ctypes.c_float, _I32,
+                                        _P, _P, _P]),
     "seer_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "seer_last_error_message": (ctypes.c_char_p, []),
     "seer_version": (ctypes.c_char_p, []),
@@ -397,6 +404,21 @@ def seer_decode_step(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w
                              threshold, max_selected, block_idx, num_selected, logits, scale,
                              num_split, workspace, out, lse)
     _check(lib().seer_decode_step(*args, _stream(q)), "seer_decode_step")
+
+
+def seer_decode_step_noalloc(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k,
+                             seq_lens, kcomp_lens, kcomp, max_new_blocks: int, rope_theta: float,
+                             mode: int, topk_blocks: int, threshold: float, max_selected: int,
+                             block_idx, num_selected, logits, scale: float, num_split: int, out,
+                             lse=None) -> None:
+    """seer_decode_step with the library's static workspace (no workspace
+    argument, nothing allocated by the call)."""
+    args = _decode_step_args(dims, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
+                             kcomp_lens, kcomp, max_new_blocks, rope_theta, mode, topk_blocks,
+                             threshold, max_selected, block_idx, num_selected, logits, scale,
+                             num_split, None, out, lse)
+    args = args[:22] + args[24:]  # without the workspace pointer and size
+    _check(lib().seer_decode_step_noalloc(*args, _stream(q)), "seer_decode_step_noalloc")
 
 
 def _decode_step_args(dims: SeerDims, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,

@@ -16,6 +16,7 @@ constexpr int kMaxNBSelect = 8192;     // blocks per sequence the select kernel 
 constexpr int kMaxSplit = 128;         // splits per (b, h) in the decode kernel
 constexpr int kDecodeMergeLds = 48 * 1024;  // LDS bytes for the decode wave merge
 constexpr int kMaxInlineNew = 4;       // new cache entries the gate launch computes itself
+constexpr size_t kNoAllocScratchBytes = SEER_NOALLOC_SCRATCH_BYTES;  // seer_decode_step_noalloc's workspace
 constexpr int kCounterBytes = 256;     // alignment of the partial outputs after the partial lse
 constexpr int kPrefillTokenTile = 64;  // prefill: key tile, and the padding of the token axis
 constexpr int kSkMaxPairs = 2048;      // (b, h) pairs the stream-K decode prefixes in LDS

@@ -23,9 +23,10 @@
  *     NULL = the default stream) and returns as soon as its kernels are
  *     queued.  No call synchronises the host with the device.
  *   - The caller owns every buffer.  The library allocates nothing and keeps
- *     no pointer after a call returns.  Outputs are fully overwritten
- *     (including padding), so callers never pre-initialise them; the only
- *     exception is the decode workspace of
+ *     no pointer after a call returns (seer_decode_step_noalloc uses a
+ *     static array of the library instead of a caller's workspace).
+ *     Outputs are fully overwritten (including padding), so callers never
+ *     pre-initialise them; the only exception is the decode workspace of
  *     seer_sparse_decode / seer_dense_decode (and their paged forms), which
  *     holds counters that must be zero before it is first used (every call
  *     leaves them zero again).  The fused step's workspace needs no
@@ -354,6 +355,40 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
                      int32_t* block_idx, int32_t* num_selected, float* logits,
                      float scale, int32_t num_split, void* workspace,
                      size_t workspace_bytes, uint16_t* out, float* lse, void* stream);
+
+/*
+ * seer_decode_step_noalloc -- seer_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and results, without
+ * the workspace.  The library keeps the workspace in a static device array
+ * of 16 MiB (SEER_NOALLOC_SCRATCH_BYTES), one per GPU, held until the
+ * process ends; the call itself allocates nothing.
+ *
+ *   The step's workspace is seer_decode_step_workspace_bytes(dims,
+ *   max_selected, num_split) bytes, exactly what a caller of
+ *   seer_decode_step would size, so both calls take the same path and give
+ *   bit-identical results.  A step that needs more than the array holds
+ *   returns SEER_ERR_WORKSPACE before any launch.
+ *
+ *   The first call on a device takes the array's device address (a host
+ *   query, no launch).  The array needs no particular contents: as in
+ *   seer_decode_step, the gate launch zeroes the decode's split counters.
+ *
+ *   Every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (other streams, other
+ *   threads, graphs replayed concurrently) race on it and must be ordered
+ *   by the caller.
+ */
+#define SEER_NOALLOC_SCRATCH_BYTES (16u << 20)
+int seer_decode_step_noalloc(const seer_dims* dims, const uint16_t* q_nope, const uint16_t* q,
+                             const uint16_t* k_nope, const uint16_t* k_cache,
+                             const uint16_t* v_cache, const uint16_t* w_q, const uint16_t* w_k,
+                             const int32_t* seq_lens, int32_t* kcomp_lens, uint16_t* kcomp,
+                             int32_t max_new_blocks, double rope_theta, int32_t mode,
+                             int32_t topk_blocks, float threshold, int32_t max_selected,
+                             int32_t* block_idx, int32_t* num_selected, float* logits,
+                             float scale, int32_t num_split, uint16_t* out, float* lse,
+                             void* stream);
 
 /*
  * seer_prefill_attention -- causal prefill attention of whole sequences (a
