@@ -110,13 +110,18 @@ def main() -> int:
                          "the benchmarked batch over a paged cache and with top-p, and the pages' "
                          "microbenchmark grid (64/8 heads, batch 1/4/16, 8k/32k/128k, "
                          "50%%/90%% sparsity)")
-    ap.add_argument("--traffic-pass", action="store_true",
-                    help="for rocprofv3 --pmc runs: a few decode launches and a plain copy of "
-                         "known size (the counters' scale), then exit")
+    ap.add_argument("--counter-pass", "--traffic-pass", dest="counter_pass", action="store_true",
+                    help="for rocprofv3 --pmc runs: launches of every kernel of the path with "
+                         "their algorithmic bytes, and a plain copy of known size (the counters' "
+                         "scale); prints one JSON line describing them, then exits")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("PASS_JSON", "FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: HBM bytes per kernel from the counter pass's JSON line and "
+                         "the FETCH_SIZE and WRITE_SIZE counter_collection CSVs of two "
+                         "--counter-pass runs; writes profiles/decode_traffic.json and prints "
+                         "a markdown table")
     args = ap.parse_args()
-    if args.traffic_pass:
-        args.replicas = min(args.replicas, 2)
-        args.warmup = max(args.warmup, 2)
+    if args.counter_summary:
+        return counter_summary(*args.counter_summary)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode path of one layer is measured on a "
@@ -135,6 +140,8 @@ def main() -> int:
     S.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.counter_pass:
+        return counter_pass(S, torch, np, dev)
     if args.prefill_only:
         print(json.dumps({"prefill_gt": prefill_leg(S, torch, dev, args.prefill_steps)}),
               flush=True)
@@ -187,9 +194,6 @@ def main() -> int:
     for i in range(args.warmup):
         step(i % R)
     torch.cuda.synchronize()
-
-    if args.traffic_pass:
-        return traffic_pass(reps, decode_only, torch, dev, L, bs, d)
 
     log(f"timing {args.steps} steps")
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -461,31 +465,205 @@ def selected_tokens(st, L, bs):
     return tot
 
 
-def traffic_pass(reps, decode_only, torch, dev, L, bs, d):
-    """Ten decode launches over the replicas, then three copies of 256 MiB
-    through torch.neg (reads 256 MiB, writes 256 MiB): under rocprofv3 --pmc
-    the copy's FETCH_SIZE / WRITE_SIZE give the counters' scale."""
-    n = 10
-    for i in range(n):
-        decode_only(i % len(reps))
+def _alg_decode(st, lens, B, Hq, Hkv, d, bs):
+    """Algorithmic bytes of one sparse decode launch: the selected K and V
+    rows, q, out, the index rows and counts."""
+    return (_selected_tokens(st, lens, bs) * 2 * d * 2 + 2 * B * Hq * d * 2
+            + B * Hkv * (st.max_selected + 1) * 4)
+
+
+def _alg_gate(lens, B, Hq, Hkv, d, dg, bs, max_sel):
+    """Algorithmic bytes of one selecting gate launch: the group's pre-RoPE
+    queries, the cached entries of every complete block, W_q once, the
+    index rows and counts written (no logits written)."""
+    g = Hq // Hkv
+    nc = int((np_floor_div(lens, bs)).sum())
+    return B * Hq * d * 2 + nc * Hkv * dg * 2 + Hkv * dg * g * d * 2 + B * Hkv * (max_sel + 1) * 4
+
+
+def np_floor_div(lens, bs):
+    import numpy as np
+    return np.asarray(lens, dtype=np.int64) // bs
+
+
+def counter_pass(S, torch, np, dev):
+    """--counter-pass: for rocprofv3 --pmc runs, one pass over every kernel
+    of the path on the benchmarked batch (and the 64-sequence threshold
+    batch), each group with its algorithmic bytes per launch, then three
+    torch.neg copies of 256 MiB (read 256 MiB, write 256 MiB each) whose
+    counts give the counters' scale.  Prints one JSON line that
+    --counter-summary reads."""
+    from workloads import WORKLOADS, make_inputs
+    groups = []
+
+    def group(label, kernel, workgroups, alg, launches):
+        groups.append({"label": label, "kernel": kernel, "workgroups": workgroups,
+                       "algorithmic_bytes_per_launch": int(alg), "launches": launches})
+
+    # ---- the benchmarked batch: cache build, fused steps, decode alone,
+    # dense decode, then the stream-K decode of a top-p 0.9 step
+    w = WORKLOADS["qwen3_14b_b16"]
+    B, Hq, Hkv, d, dg, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate, w.block_size
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
+    scale = 1.0 / math.sqrt(d)
+    log("counter pass: qwen3_14b_b16")
+    inp = make_inputs(w, device=str(dev))
+    lens = inp["seq_lens"].cpu().numpy()
+    st = S.DecodeStep(dims, mode=S.SELECT_TOPK, topk_blocks=w.topk_blocks, device=dev)
+    for _ in range(3):
+        st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    nbm = dims.nb_max
+    group("cache build (bulk, every complete block)", "prep_bulk_kernel<128, 128>",
+          B * Hkv * -(-nbm // 16),
+          int(np_floor_div(lens, bs).sum()) * Hkv * (bs * d * 2 + dg * 2) + Hkv * dg * 3 * d * 2, 3)
+    run = st.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+                       inp["seq_lens"], scale, 1, False)
+    for _ in range(10):
+        run()
     torch.cuda.synchronize()
+    group("gate, top-k 52 (128 pairs)", "gate_kernel<128, 128>", B * Hkv,
+          _alg_gate(lens, B, Hq, Hkv, d, dg, bs, st.max_selected), 10)
+    for _ in range(10):
+        S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], st.block_idx,
+                             st.num_selected, st.max_selected, scale, st.num_split, st.decode_ws,
+                             st.out, st.lse)
+    torch.cuda.synchronize()
+    group("sparse decode, top-k 52, fixed splits", "decode_kernel<128, 64, false, 8, false, false>",
+          B * Hkv * st.num_split, _alg_decode(st, lens, B, Hq, Hkv, d, bs), 20)
+    dn = _dense_buffers(S, torch, dims, dev)
+    for _ in range(3):
+        S.seer_dense_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"], scale, *dn)
+    torch.cuda.synchronize()
+    group("dense decode (baseline)", "decode_kernel<128, 64, true, 8, false, false>",
+          B * Hkv * dn[0], int(lens.sum()) * Hkv * 2 * d * 2 + 2 * B * Hq * d * 2, 3)
+    stp = S.DecodeStep(dims, mode=S.SELECT_TOPP, threshold=0.9, device=dev)
+    stp.kcomp.copy_(st.kcomp)
+    stp.kcomp_lens.copy_(st.kcomp_lens)
+    run_p = stp.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"],
+                          inp["w_k"], inp["seq_lens"], scale, 1, False)
+    for _ in range(10):
+        run_p()
+    torch.cuda.synchronize()
+    group("sparse decode, top-p 0.9, stream-K (fused step)",
+          "decode_kernel<128, 64, false, 8, false, true>", None,
+          _alg_decode(stp, lens, B, Hq, Hkv, d, bs), 10)
+    del inp, st, stp, run, run_p, dn
+    torch.cuda.empty_cache()
+
+    # ---- the 64-sequence threshold batch (b = 128, fixed splits)
+    w = WORKLOADS["threshold_b128"]
+    B, Hq, Hkv, d, dg, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate, w.block_size
+    dims = S.make_dims(B, Hq, Hkv, d, dg, bs, w.max_seq_len)
+    scale = 1.0 / math.sqrt(d)
+    log("counter pass: threshold_b128")
+    inp = make_inputs(w, device=str(dev))
+    lens = inp["seq_lens"].cpu().numpy()
+    st = S.DecodeStep(dims, mode=S.SELECT_THRESHOLD, threshold=w.tau, device=dev)
+    st.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
+    run = st.bind_step(inp["q"], inp["q"], inp["k"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+                       inp["seq_lens"], scale, 1, False)
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    group(f"gate, threshold 0.01 ({B * Hkv} pairs, b = 128)", "gate_kernel<128, 128>", B * Hkv,
+          _alg_gate(lens, B, Hq, Hkv, d, dg, bs, st.max_selected), 5)
+    group("sparse decode, threshold 0.01, b = 128, fixed splits",
+          "decode_kernel<128, 128, false", B * Hkv * st.num_split,
+          _alg_decode(st, lens, B, Hq, Hkv, d, bs), 5)
+    del inp, st, run
+    torch.cuda.empty_cache()
+
     copy_bytes = 256 << 20
     src = torch.ones(copy_bytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    per_rep = []
-    for inp, st in reps:
-        B, Hq = inp["q"].shape[0], inp["q"].shape[1]
-        idx_bytes = st.block_idx.numel() * 4 + st.num_selected.numel() * 4
-        per_rep.append(selected_tokens(st, L, bs) * 2 * d * 2 + 2 * B * Hq * d * 2 + idx_bytes)
-    alg = sum(per_rep[i % len(reps)] for i in range(n)) / n
-    print(json.dumps({"traffic_pass": True, "decode_launches": n,
-                      "decode_algorithmic_bytes_per_launch": int(alg),
-                      "copy_kernel": "neg_kernel", "copy_read_bytes": copy_bytes,
-                      "copy_write_bytes": copy_bytes, "copies": 3,
+    print(json.dumps({"counter_pass": True, "groups": groups, "copy_kernel": "neg_kernel",
+                      "copy_bytes_each_way": copy_bytes, "copies": 3,
                       "decode_src_sha256_16": decode_src_hash()}), flush=True)
+    return 0
+
+
+def _read_counters(path):
+    """{(kernel name, workgroups): [value per dispatch, in dispatch order]}
+    for the one counter of a rocprofv3 --pmc counter_collection CSV."""
+    import csv
+    import re
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = re.sub(r"^void ", "", row["Kernel_Name"])
+            name = re.sub(r"seer::\(anonymous namespace\)::|seer::", "", name)
+            wg = int(row["Grid_Size"]) // max(1, int(row["Workgroup_Size"]))
+            out.setdefault((name, wg), []).append((int(row.get("Dispatch_Id", 0) or 0),
+                                                   float(row["Counter_Value"])))
+    return {k: [v for _, v in sorted(vals)] for k, vals in out.items()}
+
+
+def counter_summary(pass_json, fetch_csv, write_csv):
+    """--counter-summary: scaled HBM bytes per launch of each group of the
+    counter pass (the mean over the group's last `launches` dispatches), the
+    counters' scale from the copy, and profiles/decode_traffic.json for the
+    benchmarked decode."""
+    with open(pass_json) as f:
+        info = next(json.loads(line) for line in f if line.startswith("{"))
+    fetch, write = _read_counters(fetch_csv), _read_counters(write_csv)
+
+    def pick(table, kernel, wg, n):
+        keys = [k for k in table if k[0].startswith(kernel) and (wg is None or k[1] == wg)]
+        if len(keys) != 1:
+            raise SystemExit(f"counter summary: {len(keys)} kernel groups match {kernel!r} "
+                             f"with {wg} workgroups: {keys}")
+        vals = table[keys[0]][-n:]
+        return sum(vals) / len(vals), keys[0]
+
+    n_copy = info["copies"]
+    copy_f = [v for k, vals in fetch.items() if info["copy_kernel"] in k[0] for v in vals][-n_copy:]
+    copy_w = [v for k, vals in write.items() if info["copy_kernel"] in k[0] for v in vals][-n_copy:]
+    cf, cw = sum(copy_f) / len(copy_f), sum(copy_w) / len(copy_w)
+    known_kib = info["copy_bytes_each_way"] / 1024
+    fs, ws_ = known_kib / cf, known_kib / cw
+    rows = []
+    for g in info["groups"]:
+        f_raw, key = pick(fetch, g["kernel"], g["workgroups"], g["launches"])
+        w_raw, _ = pick(write, g["kernel"], g["workgroups"], g["launches"])
+        fb, wb = f_raw * fs * 1024, w_raw * ws_ * 1024
+        rows.append({"label": g["label"], "kernel": key[0], "workgroups": key[1],
+                     "fetch_kib_raw": round(f_raw, 1), "write_kib_raw": round(w_raw, 1),
+                     "fetch_bytes": int(fb), "write_bytes": int(wb),
+                     "algorithmic_bytes": g["algorithmic_bytes_per_launch"],
+                     "traffic_over_algorithmic": round((fb + wb) / g["algorithmic_bytes_per_launch"],
+                                                       4)})
+    dec = next(r for r in rows if r["label"].startswith("sparse decode, top-k 52"))
+    traffic = {
+        "kernel": "decode_kernel", "workload": "qwen3_14b_b16",
+        "decode_src_sha256_16": info["decode_src_sha256_16"],
+        "fetch_kib_per_launch_raw": dec["fetch_kib_raw"],
+        "write_kib_per_launch_raw": dec["write_kib_raw"],
+        "copy_fetch_kib_raw": round(cf, 1), "copy_write_kib_raw": round(cw, 1),
+        "copy_bytes_each_way": info["copy_bytes_each_way"],
+        "fetch_scale": round(known_kib / round(cf, 1), 5),
+        "write_scale": round(known_kib / round(cw, 1), 5),
+    }
+    traffic["fetch_bytes_per_launch"] = int(round(dec["fetch_kib_raw"] * traffic["fetch_scale"] * 1024))
+    traffic["write_bytes_per_launch"] = int(round(dec["write_kib_raw"] * traffic["write_scale"] * 1024))
+    traffic["bytes_per_launch"] = traffic["fetch_bytes_per_launch"] + traffic["write_bytes_per_launch"]
+    traffic["algorithmic_bytes_per_launch"] = dec["algorithmic_bytes"]
+    traffic["traffic_over_algorithmic"] = round(traffic["bytes_per_launch"] /
+                                                dec["algorithmic_bytes"], 4)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    print(f"| kernel group | kernel | workgroups | FETCH_SIZE KiB | WRITE_SIZE KiB | "
+          f"HBM bytes (scaled) | algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['label']} | `{r['kernel']}` | {r['workgroups']} | {r['fetch_kib_raw']} | "
+              f"{r['write_kib_raw']} | {r['fetch_bytes'] + r['write_bytes']:,} | "
+              f"{r['algorithmic_bytes']:,} | {r['traffic_over_algorithmic']} |")
+    print(f"\ncopy `{info['copy_kernel']}` of {info['copy_bytes_each_way']:,} B each way: "
+          f"FETCH_SIZE {cf:.1f} KiB (scale {fs:.5f}), WRITE_SIZE {cw:.1f} KiB (scale {ws_:.5f})")
     return 0
 
 

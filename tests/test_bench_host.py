@@ -101,3 +101,49 @@ def test_cpu_baseline_scales_a_cut_sample(monkeypatch):
     assert res["pairs_timed"] == 1 < pairs
     assert 2000 * pairs <= res["value"] <= 3000 * pairs
     assert f"1 of {pairs}" in res["sample"]
+
+
+def test_counter_summary_scales_each_group(tmp_path, monkeypatch):
+    """--counter-summary on synthetic counter CSVs: each group's counters are
+    averaged over its last launches, scaled by the copy's, and the decode's
+    figures land in the traffic file with the pass's source hash."""
+    cols = ("Dispatch_Id,Grid_Size,Workgroup_Size,Kernel_Name,Counter_Name,Counter_Value")
+    kern = [("void seer::(anonymous namespace)::decode_kernel<128, 64, false, 8, false, false>"
+             "(seer::(anonymous namespace)::DecodeParams)", 256, 512),
+            ("void seer::(anonymous namespace)::gate_kernel<128, 128>(seer::GateParams)", 128, 512),
+            ("void at::native::neg_kernel(...)", 65536, 256)]
+
+    def csv_file(name, counter, values):
+        lines = [cols]
+        for i, (k, v) in enumerate(values):
+            kname, wgs, wgsz = kern[k]
+            lines.append(f'{i},{wgs * wgsz},{wgsz},"{kname}",{counter},{v}')
+        path = tmp_path / name
+        path.write_text("\n".join(lines) + "\n")
+        return str(path)
+
+    # decode: a cold first launch, then two at 100 KiB fetched / 2 written;
+    # gate: 10 / 1; the copy: 131072 KiB fetched (scale 2), 262144 written
+    fetch = csv_file("f.csv", "FETCH_SIZE", [(0, 999.0), (0, 100.0), (0, 100.0), (1, 10.0),
+                                             (2, 131072.0), (2, 131072.0), (2, 131072.0)])
+    write = csv_file("w.csv", "WRITE_SIZE", [(0, 2.0), (0, 2.0), (0, 2.0), (1, 1.0),
+                                             (2, 262144.0), (2, 262144.0), (2, 262144.0)])
+    info = {"counter_pass": True, "copy_kernel": "neg_kernel", "copy_bytes_each_way": 256 << 20,
+            "copies": 3, "decode_src_sha256_16": "abc",
+            "groups": [{"label": "sparse decode, top-k 52, fixed splits",
+                        "kernel": "decode_kernel<128, 64, false, 8, false, false>",
+                        "workgroups": 256, "algorithmic_bytes_per_launch": 200 * 1024,
+                        "launches": 2},
+                       {"label": "gate", "kernel": "gate_kernel<128, 128>", "workgroups": 128,
+                        "algorithmic_bytes_per_launch": 20 * 1024, "launches": 1}]}
+    pj = tmp_path / "pass.json"
+    pj.write_text("[bench] log line\n" + json.dumps(info) + "\n")
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench.counter_summary(str(pj), fetch, write) == 0
+    t = json.loads(out.read_text())
+    assert t["decode_src_sha256_16"] == "abc"
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+    assert t["fetch_bytes_per_launch"] == 200 * 1024  # the cold launch is not averaged in
+    assert t["write_bytes_per_launch"] == 2 * 1024
+    assert t["traffic_over_algorithmic"] == pytest.approx(202 / 200, abs=1e-4)
