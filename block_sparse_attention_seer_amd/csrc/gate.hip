@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 constexpr int kBulkBlocks = 16;
 
 template <int D, int DG>
-__global__ __launch_bounds__(256) void prep_bulk_kernel(PrepParams p) {
+__global__ __launch_bounds__(256, 4) void prep_bulk_kernel(PrepParams p) {
   __shared__ CompressSmem<D, DG, kBulkBlocks> cm;
   const int per_pair = (p.max_new + kBulkBlocks - 1) / kBulkBlocks;
   const int pair = blockIdx.x / per_pair;

@@ -59,6 +59,13 @@ __device__ __forceinline__ uint2 ld8_stream(const uint16_t* p) {
   return make_uint2(v.x, v.y);
 }
 
+// The same for 16 bytes: keys read once by the cache build.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Part m (0, 1, 2) of the exact three-way bf16 split x = q0 + q1 + q2 (+ a
 // remainder below 2^-24 |x|): q0 = bf16(x), q1 = bf16(x - q0), q2 =
 // bf16(x - q0 - q1).  Each subtraction is exact in float32 (the operands
