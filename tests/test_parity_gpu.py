@@ -529,7 +529,8 @@ def test_kcomp_bulk_and_incremental_match_oracle(S, d, dg, bs, lens):
             worst = max(worst, float((diff / ulp).max()) if diff.size else 0.0)
     say(f"kcomp d={d} dg={dg} bs={bs}: {n_off} of {n_tot} entries one bf16 step from the "
         f"float64 oracle (rate {n_off / max(1, n_tot):.2e})")
-    assert n_off <= max(2, n_tot // 500), f"{n_off} of {n_tot} entries off by one step"
+    # observed: 2 of 16640 at d = 128 (1.2e-4), none in the other cases
+    assert n_off <= max(2, n_tot // 2000), f"{n_off} of {n_tot} entries off by one step"
     # incremental: grow each sequence token by token from scratch and compare bitwise
     kl2 = torch.zeros((B,), dtype=torch.int32, device=DEV)
     kc2 = torch.zeros_like(kc)
