@@ -1007,7 +1007,8 @@ def extra_measurements(S, torch, np, dev, grid=False):
 
     # top-p over the same inputs: the fused step (whose decode divides the
     # uneven selections evenly over the grid when there are fewer pairs than
-    # compute units), then the standalone decode call with fixed splits
+    # compute units), then the standalone decode call with fixed splits and
+    # with the balanced division (SEER_SPLIT_BALANCED)
     for p_mass in (0.9, 0.99):
         stp = S.DecodeStep(dims, mode=S.SELECT_TOPP, threshold=p_mass, device=dev)
         stp.build_cache(inp["k"], inp["w_k"], inp["seq_lens"])
@@ -1020,8 +1021,14 @@ def extra_measurements(S, torch, np, dev, grid=False):
                                  stp.block_idx, stp.num_selected, stp.max_selected, scale,
                                  stp.num_split, stp.decode_ws, stp.out, stp.lse)
 
+        def dec_bal(i):
+            S.seer_sparse_decode(dims, inp["q"], inp["k"], inp["v"], inp["seq_lens"],
+                                 stp.block_idx, stp.num_selected, stp.max_selected, scale,
+                                 S.SPLIT_BALANCED, stp.decode_ws, stp.out, stp.lse)
+
         step_us = _flushed_median_us(torch, lambda i: run(), 30, flush)
         dec_us = _flushed_median_us(torch, dec_p, 30, flush)
+        bal_us = _flushed_median_us(torch, dec_bal, 30, flush)
         sel_p = _selected_tokens(stp, lens, bs)
         alg_p = sel_p * 2 * d * 2 + qo + B * Hkv * (stp.max_selected + 1) * 4
         yield f"qwen3_14b_b16_topp_{p_mass}", {
@@ -1031,6 +1038,8 @@ def extra_measurements(S, torch, np, dev, grid=False):
             "decode_fixed_splits_GBps": round(alg_p / (dec_us * 1e-6) / 1e9, 1),
             "decode_fixed_splits_frac_of_peak": round(alg_p / (dec_us * 1e-6) / 1e9 / PEAK_GBPS,
                                                       4),
+            "decode_balanced_us": round(bal_us, 2),
+            "decode_balanced_frac_of_peak": round(alg_p / (bal_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
             "selected_fraction": round(sel_p / float(lens.sum() * Hkv), 4),
             "dense_decode_us": round(t["dense"], 2),
             "speedup_vs_dense_step": round(t["dense"] / step_us, 3),

@@ -36,7 +36,7 @@ __all__ = [
     "seer_sparse_decode", "seer_dense_decode", "seer_sparse_decode_paged",
     "seer_dense_decode_paged", "seer_prefill_workspace_bytes", "seer_prefill_attention",
     "seer_decode_step_workspace_bytes",
-    "seer_decode_step", "seer_decode_step_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "seer_decode_step", "seer_decode_step_noalloc", "NOALLOC_SCRATCH_BYTES", "SPLIT_BALANCED",
     "seer_status_string", "seer_last_error_message", "seer_version",
     "DecodeStep",
 ]
@@ -49,6 +49,7 @@ SELECT_TOPK = 1
 SELECT_THRESHOLD = 2
 SELECT_TOPP = 3  # threshold carries the mass p
 NOALLOC_SCRATCH_BYTES = 16 << 20  # seer_decode_step_noalloc's static workspace per GPU
+SPLIT_BALANCED = -1  # num_split: the fused step's division of uneven selections
 
 EXPORTED_SYMBOLS = (
     "seer_kcomp_update", "seer_gate_workspace_bytes", "seer_gate_scores",
@@ -487,7 +488,12 @@ class DecodeStep:
         # the staged decode calls use the resolved split count
         self.split_request = int(num_split)
         self.num_split = seer_decode_num_split(dims, self.max_selected, num_split)
-        dws = seer_decode_workspace_bytes(dims, self.max_selected, self.num_split)
+        # the staged decode's split argument: threshold and top-p with an
+        # automatic count take the balanced division, as the fused step does
+        # (so both give the same bits); top-k keeps the resolved count
+        self.decode_split = (SPLIT_BALANCED if self.mode != SELECT_TOPK
+                             and self.split_request in (0, SPLIT_BALANCED) else self.num_split)
+        dws = seer_decode_workspace_bytes(dims, self.max_selected, self.decode_split)
         self.decode_ws = torch.zeros((max(dws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, Hq, dims.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -518,7 +524,7 @@ class DecodeStep:
         seer_select_blocks(d, self.logits, self.kcomp_lens, seq_lens, self.mode, self.topk_blocks,
                            self.threshold, self.max_selected, self.block_idx, self.num_selected)
         seer_sparse_decode(d, q, k_cache, v_cache, seq_lens, self.block_idx, self.num_selected,
-                           self.max_selected, scale, self.num_split, self.decode_ws, self.out,
+                           self.max_selected, scale, self.decode_split, self.decode_ws, self.out,
                            self.lse)
         return self.out, self.lse
 

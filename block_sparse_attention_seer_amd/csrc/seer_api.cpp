@@ -59,8 +59,8 @@ int gate_row_parts(const seer_dims* d) {
 }
 
 int resolve_split(const seer_dims* d, int max_blocks, int num_split, int* out) {
-  if (num_split < 0 || num_split > seer::kMaxSplit)
-    return fail(SEER_ERR_INVALID_ARG, "num_split must be in [0, 128]");
+  if (num_split < SEER_SPLIT_BALANCED || num_split > seer::kMaxSplit)
+    return fail(SEER_ERR_INVALID_ARG, "num_split must be SEER_SPLIT_BALANCED (-1) or in [0, 128]");
   if (num_split > 0) {
     *out = num_split;
     return SEER_OK;
@@ -70,6 +70,15 @@ int resolve_split(const seer_dims* d, int max_blocks, int num_split, int* out) {
   if (rc != SEER_OK) return rc;
   *out = seer::auto_num_split(d, max_blocks, cus);
   return SEER_OK;
+}
+
+// Whether a balanced division (SEER_SPLIT_BALANCED) runs stream-K: with
+// fewer (b, h) pairs than compute units.  With more, the dispatcher already
+// balances fixed splits, and stream-K's extra part boundaries measured
+// slower.
+bool balanced_uses_stream_k(int64_t pairs) {
+  int cus = 0;
+  return seer::device_cu_count(&cus) == SEER_OK && pairs < cus;
 }
 
 }  // namespace
@@ -162,8 +171,11 @@ size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks, in
   int s = 0;
   if (resolve_split(dims, max_blocks, num_split, &s) != SEER_OK) return 0;
   const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
-  return seer::decode_workspace_bytes(pairs, s, dims->num_q_heads / dims->num_kv_heads,
-                                      dims->head_dim);
+  const int g = dims->num_q_heads / dims->num_kv_heads;
+  size_t bytes = seer::decode_workspace_bytes(pairs, s, g, dims->head_dim);
+  if (num_split == SEER_SPLIT_BALANCED && balanced_uses_stream_k(pairs))
+    bytes = std::max(bytes, seer::decode_sk_workspace_bytes(pairs, s, g, dims->head_dim));
+  return bytes;
 }
 
 size_t seer_workspace_bytes(const seer_dims* dims, int32_t max_blocks, int32_t num_split) {
@@ -229,7 +241,11 @@ static int decode_common(const seer_dims* dims, const uint16_t* q, const uint16_
   const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;
   const int g = dims->num_q_heads / dims->num_kv_heads;
   const size_t need = seer::decode_workspace_bytes(pairs, s, g, dims->head_dim);
-  // stream-K only with the workspace it needs (the fused step provides it)
+  // a balanced division of a selection over a contiguous cache: stream-K
+  // where there are fewer pairs than compute units
+  if (num_split == SEER_SPLIT_BALANCED && block_idx != nullptr && paged == nullptr)
+    stream_k = stream_k || balanced_uses_stream_k(pairs);
+  // stream-K only with the workspace it needs
   stream_k = stream_k && workspace != nullptr &&
              workspace_bytes >= seer::decode_sk_workspace_bytes(pairs, s, g, dims->head_dim);
   if (stream_k) {
@@ -354,9 +370,8 @@ int seer_decode_step(const seer_dims* dims, const uint16_t* q_nope, const uint16
   // region.  With more pairs the dispatcher balances the fixed splits
   // itself, and stream-K's extra part boundaries measured slower.
   bool stream_k = false;
-  int cus = 0;
-  if (num_split == 0 && mode != SEER_SELECT_TOPK && seer::device_cu_count(&cus) == SEER_OK &&
-      pairs < cus) {
+  if ((num_split == 0 || num_split == SEER_SPLIT_BALANCED) && mode != SEER_SELECT_TOPK &&
+      balanced_uses_stream_k(pairs)) {
     const size_t sk_bytes =
         std::max(dec_bytes, seer::decode_sk_workspace_bytes(pairs, s, g, dims->head_dim));
     if (workspace_bytes >= sk_bytes + seer::step_gate_bytes(dims)) {
@@ -453,7 +468,7 @@ size_t seer_decode_step_workspace_bytes(const seer_dims* dims, int32_t max_selec
   std::string why;
   if (check_dims(dims, &why) != SEER_OK || max_selected < 1) return 0;
   size_t dec = seer_decode_workspace_bytes(dims, max_selected, num_split);
-  if (num_split == 0) {  // room for the stream-K decode of threshold and top-p
+  if (num_split == 0 || num_split == SEER_SPLIT_BALANCED) {  // room for the stream-K decode
     int s = 0;
     if (resolve_split(dims, max_selected, 0, &s) != SEER_OK) return 0;
     const int64_t pairs = static_cast<int64_t>(dims->batch) * dims->num_kv_heads;

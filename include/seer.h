@@ -81,6 +81,8 @@ enum {
 };
 
 enum { SEER_SELECT_TOPK = 1, SEER_SELECT_THRESHOLD = 2, SEER_SELECT_TOPP = 3 };
+/* num_split of the decode calls: the balanced division (see seer_sparse_decode). */
+enum { SEER_SPLIT_BALANCED = -1 };
 
 typedef struct seer_dims {
   int32_t batch;        /* B >= 1                                           */
@@ -199,7 +201,9 @@ int seer_select_blocks(const seer_dims* dims, const float* logits,
  * per-split partial results (lse and output of each split of each (b, h));
  * 0 bytes when the call uses one split.  `max_blocks` is max_selected
  * (sparse) or NBmax (dense); `num_split` 0 means "choose automatically"
- * (queries the current device).
+ * and SEER_SPLIT_BALANCED the balanced division of seer_sparse_decode (both
+ * query the current device; the balanced size includes the stream-K
+ * partials where that division applies).
  * The counters must be ZERO before the first call that uses a workspace;
  * every call leaves them zero again, so one zero-fill at allocation is
  * enough while the workspace serves calls of at most as many (b, h) pairs
@@ -215,7 +219,8 @@ size_t seer_decode_workspace_bytes(const seer_dims* dims, int32_t max_blocks,
  * num_split). */
 size_t seer_workspace_bytes(const seer_dims* dims, int32_t max_blocks, int32_t num_split);
 
-/* The split count a decode call will use (resolves num_split = 0). */
+/* The split count a decode call will use (resolves num_split = 0 and
+ * SEER_SPLIT_BALANCED to the automatic count). */
 int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks,
                           int32_t num_split, int32_t* num_split_out /* host */);
 
@@ -238,10 +243,18 @@ int seer_decode_num_split(const seer_dims* dims, int32_t max_blocks,
  *   q          [B, H_q, d] post-RoPE bf16.   k_cache, v_cache: layout above.
  *   block_idx  [B, H_kv, max_selected], num_selected [B, H_kv] (as written
  *              by seer_select_blocks; indices must not repeat).
- *   scale      usually 1/sqrt(d).   num_split 0 = automatic.
+ *   scale      usually 1/sqrt(d).   num_split 0 = automatic, 1 .. 128 as
+ *              given, or SEER_SPLIT_BALANCED: the division the fused step
+ *              gives threshold and top-p selections, whose pairs keep
+ *              different numbers of blocks -- with fewer (b, h) pairs than
+ *              compute units, all pairs' chunks divided evenly over the grid
+ *              (stream-K; the same bits as the fused step), otherwise the
+ *              automatic split count.  The paged and dense calls take it as
+ *              0.
  *   workspace  >= seer_decode_workspace_bytes(dims, max_selected, num_split)
  *              bytes, 256-byte aligned, counters zero (see above); may be
- *              NULL when that size is 0.
+ *              NULL when that size is 0.  A balanced call given only the
+ *              fixed-split size runs fixed splits.
  */
 int seer_sparse_decode(const seer_dims* dims, const uint16_t* q,
                        const uint16_t* k_cache, const uint16_t* v_cache,

@@ -85,10 +85,11 @@ def test_error_paths_without_gpu(S):
     # workspace too small (explicit split count, so no device query)
     rc = L.seer_sparse_decode(ctypes.byref(d), A, A, A, A, A, A, 53, 0.1, 4, A, 16, A, None, None)
     assert rc == 3
-    # num_split out of range
-    rc = L.seer_sparse_decode(ctypes.byref(d), A, A, A, A, A, A, 53, 0.1, 999, A, 10 ** 9, A,
-                              None, None)
-    assert rc == 1
+    # num_split out of range (above 128, or below SEER_SPLIT_BALANCED = -1)
+    for bad_split in (999, -2):
+        rc = L.seer_sparse_decode(ctypes.byref(d), A, A, A, A, A, A, 53, 0.1, bad_split, A,
+                                  10 ** 9, A, None, None)
+        assert rc == 1
     # select: capacity too small for top-k, bad mode, bad threshold
     rc = L.seer_select_blocks(ctypes.byref(d), A, A, A, 1, 52, 0.0, 52, A, A, None)
     assert rc == 1

@@ -548,6 +548,76 @@ def test_kcomp_bulk_and_incremental_match_oracle(S, d, dg, bs, lens):
         assert torch.equal(kc2[b, :, :n], kc[b, :, :n])
 
 
+def test_balanced_split_request(S):
+    """num_split = SEER_SPLIT_BALANCED: a selection over a contiguous cache
+    with fewer pairs than compute units is divided stream-K over the grid
+    (every pair against the oracle); given only the fixed-split workspace it
+    runs the automatic split count (the same bits as num_split = 0), and the
+    paged and dense calls take it as 0."""
+    lens = [4096, 700, 1, 3000, 64, 2500]
+    B, Hq, Hkv, d, bs = len(lens), 16, 4, 128, 64
+    say(f"balanced split request lens={lens}")
+    lmax = max(lens) + 3
+    gen = torch.Generator().manual_seed(977)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16).to(DEV)
+    k, v = make_kv(B, Hkv, lmax, d, gen, poison_from=lens)
+    kp, vp, table = to_pages(k, v, bs, gen, table_pad=0)
+    dims = S.make_dims(B, Hq, Hkv, d, d, bs, lmax)
+    nbm = dims.nb_max
+    idx, nsel = random_selection(lens, bs, Hkv, nbm, np.random.default_rng(977))
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kd, vd, kpd, vpd, td = k.to(DEV), v.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV)
+    idx_d, nsel_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(nsel).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    bal = S.SPLIT_BALANCED
+    ns = S.seer_decode_num_split(dims, nbm, bal)
+    assert ns == S.seer_decode_num_split(dims, nbm, 0)
+    big = S.seer_decode_workspace_bytes(dims, nbm, bal)
+    small = S.seer_decode_workspace_bytes(dims, nbm, 0)
+    assert big > small  # 24 pairs: the stream-K partials are included
+
+    def ws(nbytes):
+        return torch.zeros(max(nbytes, 256) // 4 + 64, dtype=torch.float32, device=DEV)
+
+    def fresh():
+        return (torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV),
+                torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV))
+
+    o_bal, l_bal = fresh()
+    S.seer_sparse_decode(dims, q, kd, vd, seq, idx_d, nsel_d, nbm, scale, bal, ws(big), o_bal,
+                         l_bal)
+    o_fb, l_fb = fresh()  # balanced request, fixed-split workspace only
+    S.seer_sparse_decode(dims, q, kd, vd, seq, idx_d, nsel_d, nbm, scale, bal, ws(small), o_fb,
+                         l_fb)
+    o_0, l_0 = fresh()
+    S.seer_sparse_decode(dims, q, kd, vd, seq, idx_d, nsel_d, nbm, scale, 0, ws(small), o_0, l_0)
+    res = {}
+    for name, split in (("bal", bal), ("auto", 0)):
+        op, lp = fresh()
+        S.seer_sparse_decode_paged(dims, q, kpd, vpd, td, seq, idx_d, nsel_d, nbm, scale, split,
+                                   ws(big), op, lp)
+        od, ld = fresh()
+        S.seer_dense_decode(dims, q, kd, vd, seq, scale, split, ws(big), od, ld)
+        res[name] = (op, lp, od, ld)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fb.view(torch.int16), o_0.view(torch.int16))
+    assert torch.equal(l_fb.view(torch.int32), l_0.view(torch.int32))
+    for a_, b_ in zip(res["bal"], res["auto"]):
+        assert torch.equal(a_.view(torch.int32) if a_.dtype == torch.float32 else a_.view(torch.int16),
+                           b_.view(torch.int32) if b_.dtype == torch.float32 else b_.view(torch.int16))
+    g = Hq // Hkv
+    og, lg = f64(o_bal), f64(l_bal)
+    for b in range(B):
+        kk_all, vv_all = f64(k[b, :, :lens[b]]), f64(v[b, :, :lens[b]])
+        for h in range(Hkv):
+            blocks = idx[b, h, :nsel[b, h]].tolist()
+            o_ref, l_ref = O.sparse_decode_pair(f64(q[b, h * g:(h + 1) * g]), kk_all[h],
+                                                vv_all[h], lens[b], blocks, bs, scale)
+            what = f"balanced b={b} h={h} ({len(blocks)} blocks)"
+            assert_out_close(og[b, h * g:(h + 1) * g], o_ref, what)
+            assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, what)
+
+
 # --------------------------------------------------------------- the gate
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,dg,bs,lens", [
@@ -828,10 +898,10 @@ def _clone_state(st_from, st_to):
 ])
 def test_fused_step_equals_staged(S, name, overrides):
     """seer_decode_step reproduces the four staged calls bit for bit.  Under
-    threshold and top-p with an automatic split count the fused decode
-    divides all pairs' chunks evenly over the grid (stream-K), which sums in
-    another order: there cache, indices and logits stay bit-identical, both
-    fused calls give the same bits, and every pair matches the oracle."""
+    threshold and top-p with an automatic split count both divide all pairs'
+    chunks evenly over the grid (stream-K; the staged decode through
+    SEER_SPLIT_BALANCED); there every pair is checked against the oracle as
+    well."""
     w = WORKLOADS[name].replace(**overrides)
     say(f"fused vs staged {name} {overrides}")
     inp = make_inputs(w, device=DEV, separate_nope=True)
@@ -861,9 +931,8 @@ def test_fused_step_equals_staged(S, name, overrides):
         assert torch.equal(a.kcomp, x.kcomp)
         assert torch.equal(a.num_selected, x.num_selected)
         assert torch.equal(a.block_idx, x.block_idx)
-        ref = b if stream_k else a
-        assert torch.equal(ref.out, x.out)
-        assert torch.equal(ref.lse, x.lse)
+        assert torch.equal(a.out, x.out)
+        assert torch.equal(a.lse, x.lse)
     assert torch.equal(a.logits, b.logits)
     assert bool((c.logits == 123.0).all())  # untouched
     # the fused workspace's split counters (its first B*Hkv ints, present
@@ -1233,7 +1302,7 @@ def test_fused_step_split_sized_workspace_skips_stream_k(S):
     """A fused-step workspace sized for the split decode alone (the size the
     query returns for an explicit split count) is still accepted under top-p
     with an automatic split: the step then keeps fixed splits and equals the
-    staged calls bit for bit."""
+    staged calls at that split count bit for bit."""
     w = WORKLOADS["qwen3_14b_b16"].replace(batch=3, mode="topp", tau=0.9)
     say("fused step with a split-sized workspace")
     inp = make_inputs(w, device=DEV, separate_nope=True)
@@ -1243,6 +1312,7 @@ def test_fused_step_split_sized_workspace_skips_stream_k(S):
     fused = S.DecodeStep(dims, **kw)
     staged = S.DecodeStep(dims, **kw)
     assert fused.split_request == 0 and fused.num_split > 1
+    staged.decode_split = staged.num_split  # the staged decode at the fixed split count
     small = S.seer_decode_step_workspace_bytes(dims, fused.max_selected, fused.num_split)
     assert small < S.seer_decode_step_workspace_bytes(dims, fused.max_selected, 0)
     fused.step_ws = torch.zeros((small + 3) // 4, dtype=torch.float32, device=DEV)
