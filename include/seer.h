@@ -330,10 +330,12 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
  * value until then and nothing else may read it in between.
  *
  * Under SEER_SELECT_THRESHOLD and SEER_SELECT_TOPP the pairs keep different
- * numbers of blocks.  With num_split = 0, fewer (b, h) pairs than compute
- * units, and a workspace of at least seer_decode_step_workspace_bytes(dims,
- * max_selected, 0), launch 2 then divides all pairs' selected chunks evenly
- * over its grid (stream-K) instead of splitting each pair num_split ways.
+ * numbers of blocks.  With num_split = 0 (or SEER_SPLIT_BALANCED), fewer
+ * (b, h) pairs than compute units, and a workspace of at least
+ * seer_decode_step_workspace_bytes(dims, max_selected, 0), launch 2 then
+ * divides all pairs' selected chunks evenly over its grid (stream-K)
+ * instead of splitting each pair num_split ways -- the division
+ * seer_sparse_decode gives with SEER_SPLIT_BALANCED, with the same bits.
  * The result equals the split decode up to summation order (the same
  * tolerance to the exact attention), and is the same from run to run.
  *
@@ -352,8 +354,9 @@ int seer_dense_decode_paged(const seer_dims* dims, const uint16_t* q, const uint
  *                    needed: the gate queries (rounded up to 256 bytes), then
  *                    the decode workspace, whose split counters launch 1
  *                    zeroes.  One workspace may serve calls of any sizes.
- *                    With num_split = 0 the size includes the stream-K
- *                    decode's per-workgroup partials; a workspace sized for
+ *                    With num_split = 0 or SEER_SPLIT_BALANCED the size
+ *                    includes the stream-K decode's per-workgroup
+ *                    partials; a workspace sized for
  *                    the split decode alone is still accepted (no stream-K).
  *   out, lse         as seer_sparse_decode.
  */
