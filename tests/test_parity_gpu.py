@@ -618,6 +618,39 @@ def test_balanced_split_request(S):
             assert_lse_close(lg[b, h * g:(h + 1) * g], l_ref, what)
 
 
+@pytest.mark.parametrize("mode", ["threshold", "topk"])
+def test_fused_step_balanced_request(S, mode):
+    """A DecodeStep asked for SEER_SPLIT_BALANCED: the fused step (which
+    passes it through) and the staged calls give the same bits, stream-K
+    under threshold with fewer pairs than compute units, the automatic
+    split count under top-k."""
+    over = dict(batch=6, max_seq_len=20000, seq_len_range=(3000, 20000))
+    if mode == "topk":
+        over.update(mode="topk", topk_blocks=40)
+    w = WORKLOADS["threshold_b128"].replace(**over)
+    say(f"fused step, balanced split request, {mode}")
+    inp = make_inputs(w, device=DEV, separate_nope=True)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.d_gate,
+                       w.block_size, w.max_seq_len)
+    kw = dict(mode=MODES[w.mode], topk_blocks=w.topk_blocks, threshold=w.tau,
+              num_split=S.SPLIT_BALANCED, device=DEV)
+    fused, staged = S.DecodeStep(dims, **kw), S.DecodeStep(dims, **kw)
+    assert fused.split_request == S.SPLIT_BALANCED
+    assert staged.decode_split == (S.SPLIT_BALANCED if mode != "topk" else staged.num_split)
+    seq = inp["seq_lens"]
+    fused.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq - w.block_size, min=0))
+    _clone_state(fused, staged)
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"], seq)
+    fused.fused_step(*args)
+    staged.step(*args)
+    torch.cuda.synchronize()
+    for name_ in ("kcomp_lens", "kcomp", "num_selected", "block_idx", "logits"):
+        assert torch.equal(getattr(fused, name_), getattr(staged, name_)), name_
+    assert torch.equal(fused.out.view(torch.int16), staged.out.view(torch.int16))
+    assert torch.equal(fused.lse.view(torch.int32), staged.lse.view(torch.int32))
+    _check_pair(w, inp, fused, w.batch - 1, w.num_kv_heads - 1, f"balanced {mode}")
+
+
 # --------------------------------------------------------------- the gate
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,dg,bs,lens", [
