@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(GateParams p) {
   __shared__ SelectSmem s_sel;
   __shared__ float s_part[kGateRows][4];         // part sums (gate query, then logits)
   __shared__ float s_qg[DG];                     // the gate query
-  __shared__ uint16_t s_new[kMaxInlineNew][DG];  // this launch's new cache entries
+  __shared__ __align__(16) uint16_t s_new[kMaxInlineNew][DG];  // this launch's new entries (read as 16-byte words)
   __shared__ CompressSmem<D, DG, kMaxInlineNew> s_cm;
 
   const int part = blockIdx.x / p.pairs;

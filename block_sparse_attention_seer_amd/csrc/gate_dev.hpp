@@ -56,7 +56,7 @@ __device__ __forceinline__ void rope_pair(double pos, double w, float lo, float 
 // MFMA B operands as they are), then, in the same bytes once every wave has
 // read them, V = W_k u.
 template <int D, int DG, int NB = 1>
-struct CompressSmem {
+struct alignas(16) CompressSmem {  // 16-byte aligned: the MFMA operands are read as 16-byte LDS words
   static_assert(NB >= 1 && NB <= 32, "up to two 16-column MFMA tiles of blocks");
   struct Pooled {
     uint16_t mx[NB][D + 8];  // rows padded (16-byte aligned, fewer bank conflicts)
