@@ -11,9 +11,11 @@
  * One decode step of one attention layer is
  *   seer_kcomp_update  -> seer_gate_scores -> seer_select_blocks
  *   -> seer_sparse_decode            (seer_dense_decode is the full baseline)
- * or the same four stages fused into fewer launches by seer_decode_step.
- * The training side has one call: seer_prefill_attention, the causal
- * prefill forward with the gate's ground truth.
+ * or the same four stages fused into two launches by seer_decode_step
+ * (seer_decode_step_noalloc: the same without a workspace argument, for
+ * callers that cannot allocate).  The training side has one call:
+ * seer_prefill_attention, the causal prefill forward with the gate's ground
+ * truth.
  *
  * Conventions shared by every call
  *   - "bf16" buffers hold raw bfloat16 bit patterns (uint16_t).
