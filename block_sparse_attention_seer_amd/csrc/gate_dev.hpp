@@ -75,8 +75,8 @@ struct alignas(16) CompressSmem {  // 16-byte aligned: the MFMA operands are rea
 // i = 0, 1, ... (Q = 64 / (D/8) token groups; a wave instruction reads Q
 // whole key rows), reduces them in i order, then the Q groups are folded by
 // butterfly exchanges (offsets D/8, 2 D/8, ...); every lane ends with the
-// same sums.  The loads of the next batch of 8 tokens per lane (possibly of
-// the next block) are in flight while a batch is reduced.  The lanes of
+// same sums.  The loads of the next batch of kPoolBatch tokens per lane
+// (possibly of the next block) are in flight while a batch is reduced.  The lanes of
 // group 0 write block n's max and min (bf16 bits) and the three bf16 parts of
 // sum / b to u.
 // Max and min are taken on order keys of the bf16 bit patterns, two
