@@ -265,8 +265,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
         sc[nt][r] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor<32>(max_xor<16>(mx));
     const float m_new = fmaxf(m_run, mx);  // finite: some tile holds a valid token
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -316,8 +315,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, const Part& p
   }
 
   // ---- merge the waves of this split
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_xor<32>(sum_xor<16>(l_run));
   if (lq == 0) {
     sm_m[w][ln] = m_run;
     sm_l[w][ln] = l_run;

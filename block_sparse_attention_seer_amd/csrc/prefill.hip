@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(PrefillParams p) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mt][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
+      tmax = max_xor<32>(tmax) * p.scale_log2;
       if constexpr (GT) {
         if (BS == kKeys) {
           if (hf == 0 && qrow < L) rrow[static_cast<int64_t>(j) * p.Lpad] = tmax;
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(PrefillParams p) {
   }
 
   if (qrow >= L) return;
-  const float lsum = l_part + __shfl_xor(l_part, 32);
+  const float lsum = sum_xor<32>(l_part);
   const float inv = 1.f / lsum;
   uint16_t* orow = p.out + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Lmax + qrow) * D;
 #pragma unroll

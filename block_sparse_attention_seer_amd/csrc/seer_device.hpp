@@ -172,6 +172,39 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
   return min(min(lane_u32(v, 0), lane_u32(v, 16)), min(lane_u32(v, 32), lane_u32(v, 48)));
 }
 
+// ---- butterfly steps across 16- and 32-lane halves without an LDS round
+// trip.  v_permlane32_swap exchanges the upper 32 lanes of its first operand
+// with the lower 32 lanes of its second; given the same value twice, every
+// lane l then holds the values of lanes l & ~32 (first result) and l | 32
+// (second result).  v_permlane16_swap does the same between the even and odd
+// 16-lane rows, for lanes l & ~16 and l | 16.  A commutative combination of
+// the two values is the step "combine with lane l ^ 16 (or 32)", with the
+// same bits as that step taken through ds_bpermute.
+struct LanePair {
+  uint32_t lo, hi;  // the values of lanes l & ~XOR and l | XOR
+};
+template <int XOR>
+__device__ __forceinline__ LanePair lanes_xor(uint32_t v) {
+  static_assert(XOR == 16 || XOR == 32, "16- or 32-lane halves");
+  if constexpr (XOR == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return LanePair{r[0], r[1]};
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return LanePair{r[0], r[1]};
+  }
+}
+template <int XOR>
+__device__ __forceinline__ float max_xor(float v) {
+  const LanePair r = lanes_xor<XOR>(__float_as_uint(v));
+  return fmaxf(__uint_as_float(r.lo), __uint_as_float(r.hi));
+}
+template <int XOR>
+__device__ __forceinline__ float sum_xor(float v) {
+  const LanePair r = lanes_xor<XOR>(__float_as_uint(v));
+  return __uint_as_float(r.lo) + __uint_as_float(r.hi);
+}
+
 // Orders the LDS accesses of one wave: the ones before complete before the
 // ones after (a wave's LDS operations are performed in issue order; this
 // keeps the compiler from moving them across).
