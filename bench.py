@@ -694,8 +694,9 @@ def counter_summary(pass_json, fetch_csv, write_csv):
         "fetch_scale": round(known_kib / round(cf, 1), 5),
         "write_scale": round(known_kib / round(cw, 1), 5),
     }
-    traffic["fetch_bytes_per_launch"] = int(round(dec["fetch_kib_raw"] * traffic["fetch_scale"] * 1024))
-    traffic["write_bytes_per_launch"] = int(round(dec["write_kib_raw"] * traffic["write_scale"] * 1024))
+    # the same bytes as the table row (unrounded scales)
+    traffic["fetch_bytes_per_launch"] = dec["fetch_bytes"]
+    traffic["write_bytes_per_launch"] = dec["write_bytes"]
     traffic["bytes_per_launch"] = traffic["fetch_bytes_per_launch"] + traffic["write_bytes_per_launch"]
     traffic["algorithmic_bytes_per_launch"] = dec["algorithmic_bytes"]
     traffic["traffic_over_algorithmic"] = round(traffic["bytes_per_launch"] /
