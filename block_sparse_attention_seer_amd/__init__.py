@@ -512,13 +512,15 @@ class DecodeStep:
                           self.dims.nb_max, self.rope_theta)
 
     def step(self, q_nope, q, k_nope, k_cache, v_cache, w_q, w_k, seq_lens,
-             scale: Optional[float] = None, update_cache: bool = True):
+             scale: Optional[float] = None, update_cache: bool = True, max_new_blocks: int = 1):
+        """The step as four staged calls (cache update of at most
+        max_new_blocks entries per pair, gate scores, selection, decode)."""
         d = self.dims
         if scale is None:
             scale = 1.0 / math.sqrt(d.head_dim)
         if update_cache:
-            seer_kcomp_update(d, k_nope, w_k, seq_lens, self.kcomp_lens, self.kcomp, 1,
-                              self.rope_theta)
+            seer_kcomp_update(d, k_nope, w_k, seq_lens, self.kcomp_lens, self.kcomp,
+                              int(max_new_blocks), self.rope_theta)
         seer_gate_scores(d, q_nope, w_q, self.kcomp, self.kcomp_lens, seq_lens, self.gate_ws,
                          self.logits, self.rope_theta)
         seer_select_blocks(d, self.logits, self.kcomp_lens, seq_lens, self.mode, self.topk_blocks,

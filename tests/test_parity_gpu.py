@@ -1012,6 +1012,71 @@ def test_fused_step_needs_no_workspace_contents(S, name, overrides):
     _check_pair(w, inp, dirty, w.batch - 1, w.num_kv_heads - 1, f"garbage workspace {name}")
 
 
+def _random_cases(n: int, seed: int):
+    """n seeded step shapes across the ranges the library accepts: d and
+    d_gate in {64, 128}, b in {64, 128}, 1 to 16 query heads per KV head,
+    ragged lengths (empty, a lone partial block, exact block multiples),
+    every selection rule and split request."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d, dg, bs = (int(rng.choice([64, 128])) for _ in range(3))
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 3, 5, 8, 16]))
+        B = int(rng.integers(1, 5))
+        lmax = int(rng.integers(2, 48)) * bs + int(rng.integers(0, bs))
+        lens = [int(x) for x in rng.integers(0, lmax + 1, size=B)]
+        lens[int(rng.integers(0, B))] = int(rng.choice([0, 1, bs, lmax, (lmax // bs) * bs]))
+        mode = str(rng.choice(["topk", "threshold", "topp"]))
+        param = {"topk": float(rng.integers(1, 12)), "threshold": float(rng.choice([0.002, 0.02])),
+                 "topp": float(rng.choice([0.5, 0.9, 0.99]))}[mode]
+        split = int(rng.choice([0, 1, 2, 3, -1]))
+        cases.append((i, d, dg, bs, hkv, g, lmax, tuple(lens), mode, param, split))
+    return cases
+
+
+@pytest.mark.parametrize("i,d,dg,bs,hkv,g,lmax,lens,mode,param,split", _random_cases(12, 20260))
+def test_fused_step_random_shapes_match_oracle(S, i, d, dg, bs, hkv, g, lmax, lens, mode, param,
+                                               split):
+    """A seeded sweep of small shapes through the fused step with distinct
+    pre- and post-RoPE inputs and a cache two blocks behind (so the step
+    computes entries itself): every pair's selection and output against the
+    oracle's whole step, and the staged calls bit for bit."""
+    w = WORKLOADS["tiny"].replace(
+        batch=len(lens), num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d, d_gate=dg,
+        block_size=bs, max_seq_len=lmax, mode=mode, seq_len=None,
+        seq_len_range=(0, lmax), planted=min(2, max(0, lmax // bs - 1)),
+        topk_blocks=int(param) if mode == "topk" else 0,
+        tau=param if mode != "topk" else 0.0, seed=31000 + i)
+    say(f"random fused step {i}: d={d} dg={dg} bs={bs} Hkv={hkv} g={g} lens={list(lens)} "
+        f"{mode} {param} split={split}")
+    seq = torch.tensor(lens, dtype=torch.int32)
+    inp = make_inputs(w, device=DEV, seq_lens=seq, separate_nope=True)
+    dims = S.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, d, dg, bs, lmax)
+    kw = dict(mode=MODES[mode], topk_blocks=w.topk_blocks, threshold=w.tau, num_split=split,
+              device=DEV)
+    st, staged = S.DecodeStep(dims, **kw), S.DecodeStep(dims, **kw)
+    seq_d = inp["seq_lens"]
+    st.build_cache(inp["k_nope"], inp["w_k"], torch.clamp(seq_d - 2 * bs, min=0))
+    _clone_state(st, staged)
+    # two blocks to add per pair; allowances of 2 to 5 (above 4 the fused
+    # step runs the staged update before its two launches)
+    args = (inp["q_nope"], inp["q"], inp["k_nope"], inp["k"], inp["v"], inp["w_q"], inp["w_k"],
+            seq_d)
+    st.fused_step(*args, max_new_blocks=2 + i % 4)
+    staged.step(*args, max_new_blocks=2 + i % 4)
+    torch.cuda.synchronize()
+    assert st.kcomp_lens.cpu().tolist() == [L // bs for L in lens]
+    # the staged calls give the same bits
+    for name_ in ("kcomp_lens", "kcomp", "num_selected", "block_idx"):
+        assert torch.equal(getattr(st, name_), getattr(staged, name_)), name_
+    assert torch.equal(st.out.view(torch.int16), staged.out.view(torch.int16))
+    assert torch.equal(st.lse.view(torch.int32), staged.lse.view(torch.int32))
+    for b in range(w.batch):
+        for h in range(hkv):
+            _check_pair(w, inp, st, b, h, f"random case {i} b={b} h={h}")
+
+
 def test_fused_step_long_row(S):
     """Rows of 100k to 147k tokens (2304 blocks per row, threshold, two fixed
     splits): cache, indices, logits and outputs of the fused step equal the
