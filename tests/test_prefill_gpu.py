@@ -121,6 +121,37 @@ def test_prefill_matches_oracle(S, d, bs, Hq, Hkv, lens):
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
+def _random_prefill_cases(n: int, seed: int):
+    """n seeded shapes: d and b in {64, 128}, 1 to 16 query heads per KV
+    head, 1 to 3 KV heads and sequences, lengths from 0 to 1200 with block
+    edges among them, and softmax scales around 1/sqrt(d)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d, bs = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+        hkv, g = int(rng.integers(1, 4)), int(rng.choice([1, 2, 3, 5, 8, 16]))
+        lens = [int(x) for x in rng.integers(1, 1201, size=int(rng.integers(1, 4)))]
+        lens[int(rng.integers(0, len(lens)))] = int(rng.choice([0, 1, bs - 1, bs, bs + 1, 4 * bs]))
+        scale = float(rng.uniform(0.5, 2.0)) / math.sqrt(d)
+        cases.append((i, d, bs, hkv * g, hkv, tuple(lens), scale))
+    return cases
+
+
+@pytest.mark.parametrize("i,d,bs,Hq,Hkv,lens,scale", _random_prefill_cases(8, 4242))
+def test_prefill_random_shapes_match_oracle(S, i, d, bs, Hq, Hkv, lens, scale):
+    """A seeded sweep of prefill shapes against the oracle, every row of
+    every head; rows past each sequence untouched."""
+    lens = list(lens)
+    say(f"random prefill {i}: d={d} bs={bs} Hq={Hq} Hkv={Hkv} lens={lens} scale={scale:.4f}")
+    w, inp = make_case(d, bs, Hq, Hkv, lens, seed=5000 + i)
+    dims = S.make_dims(w.batch, Hq, Hkv, d, d, bs, w.max_seq_len)
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    out, lse, gt = run(S, dims, dinp, scale)
+    check_against_oracle(S, w, inp, out, lse, gt, scale)
+    for b, L in enumerate(lens):
+        assert torch.all(torch.isnan(lse[b, :, L:])) and torch.all(torch.isnan(gt[b, :, L:]))
+
+
 def test_prefill_deterministic_and_tiny_workload(S):
     w = PREFILL_WORKLOADS["prefill_tiny"]
     say(f"prefill {w.name}")
