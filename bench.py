@@ -870,6 +870,15 @@ def extra_measurements(S, torch, np, dev, grid=False):
             graphs[i % 2].replay()
         graph_us = _events_us(torch, lambda i: graphs[i % 2].replay(), 100)
         del graphs
+        # eight steps (the two replicas alternating) in one graph
+        g8 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g8):
+            for i in range(8):
+                reps[i % 2][2]()
+        for _ in range(3):
+            g8.replay()
+        graph8_us = _events_us(torch, lambda i: g8.replay(), 20) / 8
+        del g8
 
         def dec(i):
             inp, st, _ = reps[i % 2]
@@ -898,6 +907,7 @@ def extra_measurements(S, torch, np, dev, grid=False):
             "head_dim": d, "block_size": bs, "mode": w.mode,
             "seq_len": int(lens[0]) if w.seq_len else [int(lens.min()), int(lens.max())],
             "step_us": round(step_us, 2), "step_us_graph_replay": round(graph_us, 2),
+            "step_us_graph_replay_8_steps_per_graph": round(graph8_us, 2),
             "decode_us": round(dec_us, 2),
             "decode_GBps": round(dec_alg / (dec_us * 1e-6) / 1e9, 1),
             "decode_frac_of_peak": round(dec_alg / (dec_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
